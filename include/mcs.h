@@ -1,0 +1,211 @@
+/*
+ * mcs.h -- C ABI of libmcs, MI355X (gfx950) token-sparse attention.
+ *
+ * The library implements the hot path of MC-Sparse ("MC-Sparse: Deconstructing
+ * and Closing the Dense-Sparse Attention Gap in Diffusion Transformers",
+ * arXiv 2610.06801), as the method is described on the ai.info summary page
+ * ("Key Contributions", "Methodology in Plain English"), the wispaper.ai
+ * explainer ("Token-level selection needs tile-aligned query groups",
+ * "Reused exact selection beats recomputed mean pooling", "Residual
+ * correction recovers the discarded tail") and the agihunt.info summary
+ * (method paragraphs).
+ *
+ * Per layer and denoising step a caller makes these calls:
+ *   anchor step:  mcs_group -> mcs_dense_attn (with lse) -> mcs_select
+ *                 -> mcs_sparse_attn (no residual) -> mcs_residual_update;
+ *                 the step's output is the dense output.
+ *   reuse step:   mcs_sparse_attn with the cached perm, kv_idx and residual.
+ *
+ * Conventions shared by every call
+ *   - Tensors are device pointers to contiguous row-major arrays.  bf16 values
+ *     are passed as their uint16_t bit patterns.  Q, K, V, O and the residual
+ *     are [B, H, N, D] (head-major, so one head's K/V is one contiguous slab).
+ *   - d.B, d.H, d.N >= 1; d.D is 64 or 128; the group size C is 64 or 128.
+ *   - G = ceil(N / C) query groups per head.  perm is int32 [B, H, N], a
+ *     permutation of 0..N-1 per head; group g of a head is
+ *     perm[g*C .. min((g+1)*C, N) - 1] (the last group may be short).
+ *   - kv_idx is int32 [B, H, G, K]: the K KV token ids of each group.
+ *   - lse is float32 [B, H, N], natural log.
+ *   - Every pointer argument that is not documented as nullable must be
+ *     non-NULL and 16-byte aligned.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it; the library never synchronises, never
+ *     creates streams and never allocates or frees device memory.  Scratch
+ *     memory is a caller-owned device workspace sized by the *_workspace
+ *     queries.  Calls are re-entrant; concurrent calls on different streams
+ *     must not share a workspace.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns a non-zero status, enqueues nothing, and
+ *     mcs_last_error() describes it.  A failed kernel launch returns
+ *     MCS_E_HIP.  Device faults surface at the caller's next synchronisation.
+ *   - Out-of-range ids in perm or kv_idx are clamped into [0, N) before use,
+ *     so they cannot cause out-of-bounds accesses; the result for such input
+ *     is unspecified.  NaN/Inf inputs propagate and are not checked.
+ */
+#ifndef MCS_H
+#define MCS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MCS_VERSION 100
+
+#if defined(__GNUC__)
+#define MCS_API __attribute__((visibility("default")))
+#else
+#define MCS_API
+#endif
+
+typedef enum {
+    MCS_OK = 0,
+    MCS_E_NULL = 1,        /* a required pointer is NULL                      */
+    MCS_E_SHAPE = 2,       /* B, H or N < 1, or sizes overflow 32-bit indexing */
+    MCS_E_HEAD_DIM = 3,    /* D is not 64 or 128                               */
+    MCS_E_GROUP_SIZE = 4,  /* C is not 64 or 128                               */
+    MCS_E_BUDGET = 5,      /* K is not in [1, N]                               */
+    MCS_E_SCALE = 6,       /* scale is not finite and > 0                      */
+    MCS_E_ALIGN = 7,       /* a pointer is not 16-byte aligned                 */
+    MCS_E_WORKSPACE = 8,   /* workspace NULL or smaller than required          */
+    MCS_E_HIP = 9,         /* a HIP launch failed                              */
+    MCS_E_ARG = 10         /* another argument is out of range                 */
+} mcs_status;
+
+typedef struct {
+    int32_t B; /* batch                      */
+    int32_t H; /* heads                      */
+    int32_t N; /* tokens per head            */
+    int32_t D; /* head dimension (64 or 128) */
+} mcs_dims;
+
+/*
+ * Dense attention with row log-sum-exp: the first pass of the two-pass exact
+ * selector and the anchor step's output (ai.info, "Methodology in Plain
+ * English": the first pass computes the dense output and row-wise
+ * log-sum-exp values).  Also the build's own dense baseline.
+ *   o[b,h,i,:] = sum_j softmax_j(scale * q_i.k_j) v_j   (no mask)
+ *   lse[b,h,i] = ln sum_j exp(scale * q_i.k_j)          (if lse != NULL)
+ * In: q, k, v bf16 [B,H,N,D].  Out: o bf16 [B,H,N,D]; lse float32 [B,H,N] or
+ * NULL.  fp32 accumulation and softmax.  o must not alias q, k or v.
+ */
+MCS_API mcs_status mcs_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          uint16_t* o, float* lse, mcs_dims d, float scale, void* stream);
+
+/*
+ * Token-sparse attention over gathered KV ids, with the optional cached
+ * residual added in the epilogue (wispaper.ai, "Token-level selection needs
+ * tile-aligned query groups": each group of C similar queries shares one
+ * selection of individually gathered KV tokens; "Residual correction
+ * recovers the discarded tail": reuse steps add the cached dense-minus-sparse
+ * residual).  For every query i of group g of head (b,h):
+ *   o[b,h,i,:] = sum_{j in kv_idx[b,h,g,:]} softmax_j(scale * q_i.k_j) v_j
+ *                (+ residual[b,h,i,:] when residual != NULL)
+ * The softmax is renormalised over the K selected keys.  The order of the
+ * ids within a group does not matter; ids should be distinct.
+ * In: q, k, v bf16 [B,H,N,D]; perm int32 [B,H,N]; kv_idx int32 [B,H,G,K];
+ * residual bf16 [B,H,N,D] or NULL.  Out: o bf16 [B,H,N,D] (every row written,
+ * since perm is a permutation).  1 <= K <= N.  o must not alias the inputs.
+ */
+MCS_API mcs_status mcs_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* perm, const int32_t* kv_idx,
+                           const uint16_t* residual, uint16_t* o, mcs_dims d,
+                           int32_t C, int32_t K, float scale, void* stream);
+
+/*
+ * The two attention calls above with a float32 output o [B,H,N,D] instead of
+ * bf16: the same kernels and arithmetic, only the final store differs (the
+ * bf16 calls store the round-to-nearest-even of exactly these values).  For
+ * callers that keep activations in fp32, and for verification.
+ */
+MCS_API mcs_status mcs_dense_attn_f32out(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 float* o, float* lse, mcs_dims d, float scale, void* stream);
+MCS_API mcs_status mcs_sparse_attn_f32out(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* perm, const int32_t* kv_idx,
+                                  const uint16_t* residual, float* o, mcs_dims d, int32_t C,
+                                  int32_t K, float scale, void* stream);
+
+/*
+ * Anchor-step residual (wispaper.ai, "Residual correction recovers the
+ * discarded tail": at an anchor the method records dense minus sparse output).
+ *   residual[e] = bf16(float(o_dense[e]) - float(o_sparse[e])),  e < n_elems
+ * In: o_dense, o_sparse bf16.  Out: residual bf16 (may alias either input).
+ * n_elems >= 1.
+ */
+MCS_API mcs_status mcs_residual_update(const uint16_t* o_dense, const uint16_t* o_sparse,
+                               uint16_t* residual, int64_t n_elems, void* stream);
+
+/*
+ * Exact KV selection, the second pass of the two-pass selector (ai.info,
+ * "Methodology in Plain English": recompute the QK scores, recover the
+ * probabilities from the first pass's LSE, aggregate them per query group and
+ * keep the top K; agihunt.info method paragraphs: the objective is the
+ * largest summed attention weight of the group within a budget of K tokens).
+ *   M[g, j] = sum_{i in group g} exp(scale * q_i.k_j - lse_i)   (fp32)
+ *   kv_idx[b,h,g,:] = the K ids j of largest M[g, j]; equal masses go to the
+ *                     smaller id; ids written in ascending order.
+ * In: q, k bf16 [B,H,N,D]; lse float32 [B,H,N] (from mcs_dense_attn); perm
+ * int32 [B,H,N].  Out: kv_idx int32 [B,H,G,K].  ws: device workspace of at
+ * least mcs_select_workspace(d, C, K) bytes (the per-group mass rows of a
+ * chunk of heads; a larger workspace processes more heads per launch).
+ */
+MCS_API mcs_status mcs_select(const uint16_t* q, const uint16_t* k, const float* lse,
+                      const int32_t* perm, int32_t* kv_idx, mcs_dims d, int32_t C,
+                      int32_t K, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Minimum workspace of mcs_select (one head's mass rows: G * N * 4 bytes). */
+MCS_API size_t mcs_select_workspace(mcs_dims d, int32_t C, int32_t K);
+
+/* Workspace that lets mcs_select process every head in one launch. */
+MCS_API size_t mcs_select_workspace_all_heads(mcs_dims d, int32_t C, int32_t K);
+
+/*
+ * Top-K of given non-negative float32 score rows, the selection step of
+ * mcs_select on its own (same rule: larger score first, equal scores to the
+ * smaller id, ids written ascending).  Scores must be >= 0 (or +0/-0).
+ * In: scores float32 [rows, n].  Out: idx int32 [rows, K].  1 <= K <= n.
+ */
+MCS_API mcs_status mcs_topk(const float* scores, int32_t* idx, int64_t rows, int32_t n,
+                    int32_t K, void* stream);
+
+/*
+ * Median-split PDDP grouping (ai.info, "Key Contributions" and "Methodology in
+ * Plain English"; wispaper.ai, "Token-level selection needs tile-aligned query
+ * groups": recursively project each group on its principal direction and
+ * split the ordered queries at the median until every group holds exactly C
+ * queries; batched power iteration over all heads at each tree depth).
+ * Per head, a node of n queries forms g = ceil(n/C) groups; if g > 1 its
+ * queries are ordered by (projection on the node's principal direction, query
+ * id) and the first C*floor(g/2) form the left child, the rest the right
+ * child.  Leaves are written left-first, so group g is perm[g*C ..].  The
+ * principal direction comes from power_iters steps of power iteration on the
+ * node's covariance (power_iters <= 0 selects the default, 32), started from
+ * the covariance column of largest diagonal, sign fixed so that its
+ * largest-magnitude component is positive.  Covariance, power iteration and
+ * projections are fp32.
+ * In: q bf16 [B,H,N,D].  Out: perm int32 [B,H,N].  ws: device workspace of at
+ * least mcs_group_workspace(d, C) bytes.
+ */
+MCS_API mcs_status mcs_group(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C,
+                     int32_t power_iters, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace of mcs_group in bytes (per-query projections and ids, per-node
+ * directions, and partial moments of the large nodes near the root). */
+MCS_API size_t mcs_group_workspace(mcs_dims d, int32_t C);
+
+/* Static description of a status code. */
+MCS_API const char* mcs_status_string(mcs_status s);
+
+/* Detail of the last failed call on the calling thread ("" if none). */
+MCS_API const char* mcs_last_error(void);
+
+/* MCS_VERSION of the built library. */
+MCS_API int32_t mcs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MCS_H */

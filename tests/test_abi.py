@@ -1,0 +1,148 @@
+"""The C-ABI library loads on the host and exports what include/mcs.h declares.
+
+No kernel is launched here: the only calls made are the pure host functions
+(version, status strings, workspace queries) and calls whose arguments fail
+validation, which the library rejects before touching HIP.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mcs.h")
+LIB = os.path.join(ROOT, "token_sparse_attention_amd", "libmcs.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmcs.so not built")
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared():
+    return re.findall(r"MCS_API\s+[\w\s\*]+?\b(mcs_\w+)\s*\(", _header())
+
+
+def _status_codes():
+    return {m[0]: int(m[1]) for m in re.findall(r"(MCS_\w+)\s*=\s*(\d+)", _header())}
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    lib = ctypes.CDLL(LIB)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    lib.mcs_dense_attn.argtypes = [P, P, P, P, P, Dims, F, P]
+    lib.mcs_sparse_attn.argtypes = [P, P, P, P, P, P, P, Dims, I32, I32, F, P]
+    lib.mcs_dense_attn_f32out.argtypes = [P, P, P, P, P, Dims, F, P]
+    lib.mcs_sparse_attn_f32out.argtypes = [P, P, P, P, P, P, P, Dims, I32, I32, F, P]
+    lib.mcs_residual_update.argtypes = [P, P, P, I64, P]
+    lib.mcs_select.argtypes = [P, P, P, P, P, Dims, I32, I32, F, P, SZ, P]
+    lib.mcs_topk.argtypes = [P, P, I64, I32, I32, P]
+    lib.mcs_group.argtypes = [P, P, Dims, I32, I32, P, SZ, P]
+    lib.mcs_group_workspace.argtypes = [Dims, I32]
+    lib.mcs_group_workspace.restype = SZ
+    lib.mcs_select_workspace.argtypes = [Dims, I32, I32]
+    lib.mcs_select_workspace.restype = SZ
+    lib.mcs_select_workspace_all_heads.argtypes = [Dims, I32, I32]
+    lib.mcs_select_workspace_all_heads.restype = SZ
+    lib.mcs_status_string.restype = ctypes.c_char_p
+    lib.mcs_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 14, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    ver = int(re.search(r"#define MCS_VERSION (\d+)", _header()).group(1))
+    assert lib.mcs_version() == ver
+    codes = _status_codes()
+    assert codes["MCS_OK"] == 0
+    seen = set()
+    for name, v in codes.items():
+        s = lib.mcs_status_string(v).decode()
+        assert s and s != "unknown status", name
+        seen.add(s)
+    assert len(seen) == len(codes)
+    assert lib.mcs_status_string(999).decode() == "unknown status"
+
+
+# fake, 16-byte aligned, never dereferenced: every call below fails validation first
+A, B_, C_, D_, E_ = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def _codes():
+    return _status_codes()
+
+
+def test_dense_validation(lib):
+    c = _codes()
+    d = Dims(1, 2, 100, 128)
+    assert lib.mcs_dense_attn(None, B_, C_, D_, None, d, 0.1, None) == c["MCS_E_NULL"]
+    assert b"q is NULL" in lib.mcs_last_error()
+    assert lib.mcs_dense_attn(A + 2, B_, C_, D_, None, d, 0.1, None) == c["MCS_E_ALIGN"]
+    assert lib.mcs_dense_attn(A, B_, C_, D_, E_ + 4, d, 0.1, None) == c["MCS_E_ALIGN"]
+    assert lib.mcs_dense_attn(A, B_, C_, D_, None, Dims(1, 2, 100, 96), 0.1, None) == c["MCS_E_HEAD_DIM"]
+    assert lib.mcs_dense_attn(A, B_, C_, D_, None, Dims(0, 2, 100, 64), 0.1, None) == c["MCS_E_SHAPE"]
+    assert lib.mcs_dense_attn(A, B_, C_, D_, None, Dims(1, 1 << 16, 100, 64), 0.1, None) == c["MCS_E_SHAPE"]
+    assert lib.mcs_dense_attn(A, B_, C_, D_, None, Dims(1, 40, 1 << 26, 64), 0.1, None) == c["MCS_E_SHAPE"]
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.mcs_dense_attn(A, B_, C_, D_, None, d, bad, None) == c["MCS_E_SCALE"]
+    assert lib.mcs_dense_attn_f32out(A, B_, C_, None, None, d, 0.1, None) == c["MCS_E_NULL"]
+    assert b"mcs_dense_attn_f32out: o is NULL" in lib.mcs_last_error()
+
+
+def test_sparse_validation(lib):
+    c = _codes()
+    d = Dims(1, 2, 100, 64)
+    args = lambda **kw: [kw.get(k, v) for k, v in
+                         dict(q=A, k=B_, v=C_, perm=D_, idx=E_, res=None, o=0x60000).items()]
+    assert lib.mcs_sparse_attn(*args(perm=None), d, 64, 10, 0.1, None) == c["MCS_E_NULL"]
+    assert lib.mcs_sparse_attn(*args(idx=None), d, 64, 10, 0.1, None) == c["MCS_E_NULL"]
+    assert lib.mcs_sparse_attn(*args(res=0x70008), d, 64, 10, 0.1, None) == c["MCS_E_ALIGN"]
+    assert lib.mcs_sparse_attn(*args(), d, 32, 10, 0.1, None) == c["MCS_E_GROUP_SIZE"]
+    assert lib.mcs_sparse_attn(*args(), d, 64, 0, 0.1, None) == c["MCS_E_BUDGET"]
+    assert lib.mcs_sparse_attn(*args(), d, 64, 101, 0.1, None) == c["MCS_E_BUDGET"]
+    assert lib.mcs_sparse_attn(*args(), d, 64, 10, -0.1, None) == c["MCS_E_SCALE"]
+    assert lib.mcs_sparse_attn_f32out(*args(o=0x60004), d, 64, 10, 0.1, None) == c["MCS_E_ALIGN"]
+
+
+def test_select_group_topk_residual_validation(lib):
+    c = _codes()
+    d = Dims(1, 2, 1000, 128)
+    need = lib.mcs_select_workspace(d, 128, 100)
+    assert need == 8 * 1000 * 4
+    assert lib.mcs_select_workspace_all_heads(d, 128, 100) == 2 * need
+    assert lib.mcs_select(A, B_, C_, D_, E_, d, 128, 100, 0.1, None, need, None) == c["MCS_E_WORKSPACE"]
+    assert lib.mcs_select(A, B_, C_, D_, E_, d, 128, 100, 0.1, 0x80000, need - 1, None) == c["MCS_E_WORKSPACE"]
+    assert lib.mcs_select(A, B_, None, D_, E_, d, 128, 100, 0.1, 0x80000, need, None) == c["MCS_E_NULL"]
+    gws = lib.mcs_group_workspace(d, 128)
+    assert gws >= 2 * 2 * 1000 * 4
+    assert lib.mcs_group(A, B_, d, 128, 0, 0x80000, gws - 1, None) == c["MCS_E_WORKSPACE"]
+    assert lib.mcs_group(A, B_, d, 128, 5000, 0x80000, gws, None) == c["MCS_E_ARG"]
+    assert lib.mcs_group(A, B_, d, 100, 0, 0x80000, gws, None) == c["MCS_E_GROUP_SIZE"]
+    assert lib.mcs_group_workspace(Dims(1, 2, 1000, 128), 100) == 0
+    assert lib.mcs_topk(A, B_, 0, 10, 5, None) == c["MCS_E_SHAPE"]
+    assert lib.mcs_topk(A, B_, 3, 10, 11, None) == c["MCS_E_BUDGET"]
+    assert lib.mcs_topk(None, B_, 3, 10, 5, None) == c["MCS_E_NULL"]
+    assert lib.mcs_residual_update(A, B_, C_, 0, None) == c["MCS_E_SHAPE"]
+    assert lib.mcs_residual_update(A, B_ + 8, C_, 10, None) == c["MCS_E_ALIGN"]
+
+
+def test_group_workspace_grows_with_partials(lib):
+    # large nodes near the root keep partial moments; small problems need none
+    small = lib.mcs_group_workspace(Dims(1, 1, 1024, 64), 64)
+    assert small >= 8 * 1024
+    large = lib.mcs_group_workspace(Dims(1, 40, 75600, 128), 128)
+    assert large > 8 * 40 * 75600 + 40 * 37 * (128 * 128 + 128) * 4

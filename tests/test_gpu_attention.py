@@ -1,0 +1,129 @@
+"""GPU parity of mcs_dense_attn, mcs_sparse_attn and mcs_residual_update.
+
+Every GPU call goes through the C ABI (via the ctypes binding); the expected
+values come from the fp64 oracle on the very same bf16 inputs.  Shapes span
+several tiles with ragged tails (N, K not multiples of the 64-key tile, a short
+last query group), both head dimensions and both group sizes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_sparse_attention_amd import accounting, synth
+from tests.helpers import (assert_output_close, bf16_to_f64, to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mcs():
+    from token_sparse_attention_amd import binding
+    return binding
+
+
+def _qkv(B, H, N, D, seed, scale=1.0):
+    q = synth.gaussian((B, H, N, D), seed, scale)
+    k = synth.gaussian((B, H, N, D), seed + 1, scale)
+    v = synth.gaussian((B, H, N, D), seed + 2)
+    return q, k, v
+
+
+@pytest.mark.parametrize("B,H,N,D", [(1, 2, 1000, 128), (2, 1, 333, 64), (1, 1, 37, 128), (1, 3, 1, 64),
+                                     (1, 1, 129, 64), (1, 1, 64, 128)])
+def test_dense_matches_oracle(mcs, B, H, N, D):
+    q, k, v = _qkv(B, H, N, D, seed=N + D, scale=1.5)
+    scale = 1 / math.sqrt(D)
+    o, lse = mcs.dense_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), scale, want_lse=True)
+    o_nolse = mcs.dense_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), scale)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle.dense_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), scale)
+    assert_output_close(bf16_to_f64(o), ref_o, "dense O")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=2e-3)
+    assert torch.equal(o, o_nolse)
+
+
+def test_dense_large_logits(mcs):
+    # peaked softmax: scores of order 50
+    q, k, v = _qkv(1, 1, 300, 64, seed=77, scale=3.0)
+    o, lse = mcs.dense_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), 1.0, want_lse=True)
+    ref_o, ref_lse = oracle.dense_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), 1.0)
+    assert_output_close(bf16_to_f64(o), ref_o, "dense O")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=2e-3)
+
+
+SPARSE_CASES = [
+    # B, H, N, D, C, K
+    (1, 2, 1000, 128, 128, 200),
+    (1, 1, 1000, 128, 64, 65),
+    (2, 1, 700, 64, 64, 257),
+    (1, 2, 513, 64, 128, 1),
+    (1, 1, 300, 128, 128, 300),
+    (1, 1, 50, 64, 64, 7),
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,C,K", SPARSE_CASES)
+@pytest.mark.parametrize("with_res", [False, True])
+def test_sparse_matches_oracle(mcs, B, H, N, D, C, K, with_res):
+    q, k, v = _qkv(B, H, N, D, seed=3 * N + K, scale=1.5)
+    G = accounting.num_groups(N, C)
+    perm = synth.random_perm(B, H, N, seed=N)
+    idx = synth.random_index_sets(B, H, G, K, N, seed=K)
+    res = synth.gaussian((B, H, N, D), seed=11, scale=0.1) if with_res else None
+    scale = 1 / math.sqrt(D)
+    o = mcs.sparse_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), to_dev(perm), to_dev(idx), C,
+                        residual=to_dev_bf16(res) if with_res else None, scale=scale)
+    ref = oracle.sparse_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), perm, idx, C, scale,
+                                     residual=synth.to_f64(res) if with_res else None)
+    assert_output_close(bf16_to_f64(o), ref, "sparse O")
+
+
+def test_sparse_unsorted_ids_and_full_budget(mcs):
+    B, H, N, D, C = 1, 1, 400, 128, 128
+    q, k, v = _qkv(B, H, N, D, seed=5, scale=1.5)
+    G = accounting.num_groups(N, C)
+    perm = synth.random_perm(B, H, N, seed=6)
+    idx = synth.random_index_sets(B, H, G, 150, N, seed=7)
+    shuffled = np.ascontiguousarray(idx[..., ::-1])
+    dq, dk, dv = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    a = mcs.sparse_attn(dq, dk, dv, to_dev(perm), to_dev(idx), C)
+    b = mcs.sparse_attn(dq, dk, dv, to_dev(perm), to_dev(shuffled), C)
+    ref = oracle.sparse_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), perm, idx, C, 1 / math.sqrt(D))
+    assert_output_close(bf16_to_f64(a), ref)
+    assert_output_close(bf16_to_f64(b), ref)
+    # K = N: every group attends to all keys -> dense attention
+    full = np.broadcast_to(np.arange(N, dtype=np.int32), (B, H, G, N)).copy()
+    o_full = mcs.sparse_attn(dq, dk, dv, to_dev(perm), to_dev(full), C)
+    o_dense = mcs.dense_attn(dq, dk, dv)
+    ref_dense, _ = oracle.dense_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), 1 / math.sqrt(D))
+    assert_output_close(bf16_to_f64(o_full), ref_dense)
+    assert_output_close(bf16_to_f64(o_full), bf16_to_f64(o_dense), "sparse(K=N) vs dense")
+
+
+def test_residual_update_exact(mcs):
+    a = synth.gaussian((3, 1001), seed=21)
+    b = synth.gaussian((3, 1001), seed=22, scale=0.5)
+    r = mcs.residual_update(to_dev_bf16(a), to_dev_bf16(b))
+    # exact: bf16 round-to-nearest-even of the fp32 difference of two bf16 values
+    expect = synth.to_bf16_bits((synth.to_f32(a) - synth.to_f32(b)).astype(np.float32))
+    got = r.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, expect)
+
+
+def test_anchor_identity_on_gpu(mcs):
+    # with the anchor's own inputs, sparse + residual reproduces the dense output
+    B, H, N, D, C, K = 1, 2, 640, 64, 64, 128
+    q, k, v = _qkv(B, H, N, D, seed=31, scale=1.5)
+    G = accounting.num_groups(N, C)
+    dq, dk, dv = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    perm = to_dev(synth.random_perm(B, H, N, seed=32))
+    idx = to_dev(synth.random_index_sets(B, H, G, K, N, seed=33))
+    o_dense = mcs.dense_attn(dq, dk, dv)
+    o_sp = mcs.sparse_attn(dq, dk, dv, perm, idx, C)
+    res = mcs.residual_update(o_dense, o_sp)
+    o_reuse = mcs.sparse_attn(dq, dk, dv, perm, idx, C, residual=res)
+    diff = (o_reuse.float() - o_dense.float()).abs().max().item()
+    assert diff <= 2e-2

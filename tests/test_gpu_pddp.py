@@ -1,0 +1,88 @@
+"""GPU parity of mcs_group (median-split PDDP).
+
+Group sizes must match exactly (a permutation, groups of C, one short last
+group by construction of perm), and the within-group variance W of the GPU's
+grouping must be within 1% of the oracle's (exact eigenvectors).  Closed-form
+cases (collinear queries, identical queries, separated clusters) must match
+exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from token_sparse_attention_amd import synth
+from tests.helpers import assert_perm, to_dev_bf16, within_group_variance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mcs():
+    from token_sparse_attention_amd import binding
+    return binding
+
+
+def _groups(perm, C):
+    return [set(perm[g:g + C].tolist()) for g in range(0, len(perm), C)]
+
+
+def test_collinear_queries_split_into_sorted_chunks(mcs):
+    N, D, C = 256, 64, 64
+    t = np.random.default_rng(1).permutation(N).astype(np.float32)
+    q = np.zeros((1, 1, N, D), dtype=np.float32)
+    q[0, 0, :, 0] = t                           # integers <= 255 are exact in bf16
+    perm = mcs.group(to_dev_bf16(synth.to_bf16_bits(q)), C).cpu().numpy()[0, 0]
+    order = np.argsort(t)
+    assert _groups(perm, C) == [set(order[i:i + C].tolist()) for i in range(0, N, C)]
+
+
+def test_identical_queries_keep_id_order(mcs):
+    q = np.ones((1, 2, 640, 128), dtype=np.float32)
+    perm = mcs.group(to_dev_bf16(synth.to_bf16_bits(q)), 128).cpu().numpy()
+    np.testing.assert_array_equal(perm[0, 0], np.arange(640))
+    np.testing.assert_array_equal(perm[0, 1], np.arange(640))
+
+
+def test_separated_clusters_recovered(mcs):
+    rng = np.random.default_rng(3)
+    C, G, D = 64, 8, 64
+    centres = 20.0 * rng.standard_normal((G, D))
+    label = rng.permutation(np.repeat(np.arange(G), C))
+    q = (centres[label] + 0.1 * rng.standard_normal((G * C, D))).astype(np.float32)[None, None]
+    perm = mcs.group(to_dev_bf16(synth.to_bf16_bits(q)), C).cpu().numpy()[0, 0]
+    for g in _groups(perm, C):
+        assert len(set(label[list(g)].tolist())) == 1
+
+
+@pytest.mark.parametrize("name,N,heads", [("tiny", 1024, 2), ("small", 4096, 1), ("small", 5000, 1),
+                                          ("asset3d", 3000, 2)])
+def test_within_group_variance_within_one_percent(mcs, name, N, heads):
+    w = synth.WORKLOADS[name]
+    x = synth.generate(name, heads=[(0, h) for h in range(heads)])
+    q = np.ascontiguousarray(x["q"][:, :, :N])
+    perm = mcs.group(to_dev_bf16(q), w.C).cpu().numpy()
+    assert_perm(perm)
+    qf = synth.to_f64(q)
+    for h in range(heads):
+        ref = oracle.pddp(qf[0, h], w.C)
+        w_ref = oracle.within_group_variance(qf[0, h], ref, w.C)
+        w_gpu = within_group_variance(qf[0, h], perm[0, h], w.C)
+        assert abs(w_gpu - w_ref) <= 0.01 * w_ref, (w_gpu, w_ref)
+
+
+def test_power_iteration_count_argument(mcs):
+    x = synth.generate("tiny", heads=[(0, 0)])
+    dq = to_dev_bf16(x["q"])
+    a = mcs.group(dq, 64, power_iters=0).cpu().numpy()
+    b = mcs.group(dq, 64, power_iters=32).cpu().numpy()
+    c = mcs.group(dq, 64, power_iters=64).cpu().numpy()
+    np.testing.assert_array_equal(a, b)          # 0 selects the default (32)
+    assert_perm(c)
+
+
+def test_deterministic(mcs):
+    x = synth.generate("tiny")
+    dq = to_dev_bf16(x["q"])
+    a = mcs.group(dq, 64).cpu().numpy()
+    b = mcs.group(dq, 64).cpu().numpy()
+    np.testing.assert_array_equal(a, b)

@@ -1,0 +1,106 @@
+"""GPU parity of mcs_topk (bit-exact) and mcs_select (the index criterion).
+
+mcs_topk is compared decision-for-decision with the oracle's top-K applied to
+the same float32 score rows (both sides decide in float32), including rows
+with many ties.  mcs_select is compared with the oracle's fp64 selection on
+the same groups: the ids may differ only among masses within 1e-6 of the K-th
+largest, and the retained mass must agree to 1e-4 relative.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_sparse_attention_amd import accounting, synth
+from tests.helpers import assert_index_sets_match, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mcs():
+    from token_sparse_attention_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("rows,n,K", [(3, 1, 1), (5, 1000, 1), (5, 1000, 1000), (7, 1000, 333),
+                                      (4, 5000, 1024), (2, 75600, 15104), (3, 4097, 4096)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_bit_exact(mcs, rows, n, K, ties):
+    scores = synth.mass_rows(rows, n, seed=n + K, ties=ties)
+    got = mcs.topk(to_dev(scores), K).cpu().numpy()
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r], oracle.topk_indices(scores[r], K))
+
+
+def test_topk_all_equal_and_zero(mcs):
+    scores = np.zeros((2, 300), dtype=np.float32)
+    scores[1] = 0.25
+    got = mcs.topk(to_dev(scores), 100).cpu().numpy()
+    np.testing.assert_array_equal(got[0], np.arange(100))
+    np.testing.assert_array_equal(got[1], np.arange(100))
+
+
+def _select_case(mcs, B, H, N, D, C, K, seed, perm_kind="random"):
+    q = synth.gaussian((B, H, N, D), seed, 1.5)
+    k = synth.gaussian((B, H, N, D), seed + 1, 1.5)
+    scale = 1 / math.sqrt(D)
+    qf, kf = synth.to_f64(q), synth.to_f64(k)
+    if perm_kind == "random":
+        perm = synth.random_perm(B, H, N, seed=seed)
+    else:
+        perm = oracle.pddp_bh(qf, C).astype(np.int32)
+    _, lse = oracle.dense_attention_bh(qf, kf, qf, scale)
+    ref_idx, ref_mass = oracle.select_bh(qf, kf, lse, perm, C, K, scale)
+    got = mcs.select(to_dev_bf16(q), to_dev_bf16(k), to_dev(lse.astype(np.float32)), to_dev(perm), C, K, scale)
+    got = got.cpu().numpy()
+    G = accounting.num_groups(N, C)
+    assert got.shape == (B, H, G, K)
+    for b in range(B):
+        for h in range(H):
+            assert_index_sets_match(got[b, h], ref_idx[b, h], ref_mass[b, h], K)
+
+
+@pytest.mark.parametrize("B,H,N,D,C,K", [(1, 2, 1000, 128, 128, 200), (1, 1, 700, 64, 64, 65),
+                                         (2, 1, 333, 64, 128, 1), (1, 1, 256, 128, 64, 256)])
+def test_select_matches_oracle(mcs, B, H, N, D, C, K):
+    _select_case(mcs, B, H, N, D, C, K, seed=N + K)
+
+
+def test_select_on_oracle_groups(mcs):
+    _select_case(mcs, 1, 1, 1024, 64, 64, 256, seed=5, perm_kind="pddp")
+
+
+def test_select_small_workspace_chunks_heads(mcs):
+    B, H, N, D, C, K = 1, 3, 300, 64, 64, 50
+    q = synth.gaussian((B, H, N, D), 40, 1.5)
+    k = synth.gaussian((B, H, N, D), 41, 1.5)
+    perm = synth.random_perm(B, H, N, seed=42)
+    qf, kf = synth.to_f64(q), synth.to_f64(k)
+    _, lse = oracle.dense_attention_bh(qf, kf, qf, 0.125)
+    dq, dk, dl, dp = to_dev_bf16(q), to_dev_bf16(k), to_dev(lse.astype(np.float32)), to_dev(perm)
+    one_head = mcs.select_workspace_bytes(q.shape, C, K, all_heads=False)
+    ws = torch.empty(one_head + 100, dtype=torch.uint8, device=dq.device)
+    a = mcs.select(dq, dk, dl, dp, C, K, 0.125, workspace=ws)
+    b = mcs.select(dq, dk, dl, dp, C, K, 0.125)
+    assert torch.equal(a, b)
+
+
+def test_select_with_gpu_lse(mcs):
+    # pass 1 on the GPU feeds pass 2 on the GPU; the oracle runs both passes itself
+    B, H, N, D, C, K = 1, 2, 777, 128, 128, 150
+    q = synth.gaussian((B, H, N, D), 50, 1.5)
+    k = synth.gaussian((B, H, N, D), 51, 1.5)
+    v = synth.gaussian((B, H, N, D), 52)
+    perm = synth.random_perm(B, H, N, seed=53)
+    scale = 1 / math.sqrt(D)
+    dq, dk, dv = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    _, lse = mcs.dense_attn(dq, dk, dv, scale, want_lse=True)
+    got = mcs.select(dq, dk, lse, to_dev(perm), C, K, scale).cpu().numpy()
+    qf, kf = synth.to_f64(q), synth.to_f64(k)
+    _, ref_lse = oracle.dense_attention_bh(qf, kf, synth.to_f64(v), scale)
+    ref_idx, ref_mass = oracle.select_bh(qf, kf, ref_lse, perm, C, K, scale)
+    for h in range(H):
+        assert_index_sets_match(got[0, h], ref_idx[0, h], ref_mass[0, h], K)

@@ -1,0 +1,181 @@
+"""Parity at the full sizes of the five workloads, in the launch configuration
+the benchmark times (all heads in one call).
+
+The oracle cannot redo whole heads at N = 75600 in seconds, so it checks
+sampled outputs it can compute one by one: query rows of the dense output,
+whole query groups of the sparse output, the top-K of sampled groups, and the
+within-group variance of sampled heads.  The tiny workload is checked in full.
+GPU outputs are requested in fp32 where compared with the oracle (the bf16
+outputs are checked to be exactly their round-to-nearest-even).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_sparse_attention_amd import accounting, synth
+from tests.helpers import (assert_index_sets_match, assert_output_close, assert_perm, to_dev,
+                           to_dev_bf16, within_group_variance)
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = ["tiny", "small", "large", "long", "asset3d"]
+_CACHE = {}
+
+
+@pytest.fixture(scope="module")
+def mcs():
+    from token_sparse_attention_amd import binding
+    return binding
+
+
+def _inputs(name):
+    if name not in _CACHE:
+        _CACHE.clear()            # keep one workload's tensors alive at a time
+        print(f"[workload] generating {name}", flush=True)
+        x = synth.generate(name)
+        _CACHE[name] = {"x": x, "dev": {t: to_dev_bf16(x[t]) for t in "qkv"}}
+    return _CACHE[name]
+
+
+def _sample_heads(w):
+    BH = w.B * w.H
+    return sorted({0, BH - 1}) if BH > 1 else [0]
+
+
+def _f64_head(x, t, bh, w):
+    b, h = divmod(bh, w.H)
+    return synth.to_f64(x[t][b, h])
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_dense_sampled_rows(mcs, name):
+    w = synth.WORKLOADS[name]
+    d = _inputs(name)
+    scale = 1 / math.sqrt(w.D)
+    o32, lse = mcs.dense_attn(d["dev"]["q"], d["dev"]["k"], d["dev"]["v"], scale, want_lse=True,
+                              out_dtype=torch.float32)
+    o16 = mcs.dense_attn(d["dev"]["q"], d["dev"]["k"], d["dev"]["v"], scale)
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    o32 = o32.view(-1, w.N, w.D)
+    lse = lse.view(-1, w.N)
+    rng = np.random.default_rng(w.N)
+    for bh in _sample_heads(w):
+        rows = np.unique(np.r_[0, w.N - 1, rng.choice(w.N, 62, replace=False)]) if w.N > 64 else np.arange(w.N)
+        q, k, v = (_f64_head(d["x"], t, bh, w) for t in "qkv")
+        ref_o, ref_lse = oracle.dense_attention(q[rows], k, v, scale)
+        assert_output_close(o32[bh, rows].cpu().numpy(), ref_o, f"{name} dense head {bh}")
+        np.testing.assert_allclose(lse[bh, rows].cpu().numpy(), ref_lse, rtol=0, atol=2e-3)
+
+
+def _sparse_cases():
+    for name in WORKLOADS:
+        for s in synth.WORKLOADS[name].densities:
+            yield name, s
+
+
+@pytest.mark.parametrize("name,density", list(_sparse_cases()))
+def test_sparse_reuse_sampled_groups(mcs, name, density):
+    w = synth.WORKLOADS[name]
+    d = _inputs(name)
+    K = accounting.k_from_density(density, w.N)
+    G = accounting.num_groups(w.N, w.C)
+    scale = 1 / math.sqrt(w.D)
+    perm = synth.random_perm(w.B, w.H, w.N, seed=w.cfg_id)
+    idx = synth.stratified_index_sets(w.B, w.H, G, K, w.N, seed=w.cfg_id + 100)
+    res = synth.gaussian((w.B, w.H, w.N, w.D), seed=w.cfg_id + 200, scale=0.1)
+    dperm, didx, dres = to_dev(perm), to_dev(idx), to_dev_bf16(res)
+    o32 = mcs.sparse_attn(d["dev"]["q"], d["dev"]["k"], d["dev"]["v"], dperm, didx, w.C, residual=dres,
+                          scale=scale, out_dtype=torch.float32)
+    o16 = mcs.sparse_attn(d["dev"]["q"], d["dev"]["k"], d["dev"]["v"], dperm, didx, w.C, residual=dres,
+                          scale=scale)
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    o32 = o32.view(-1, w.N, w.D).cpu().numpy()
+    permf, idxf, resf = perm.reshape(-1, w.N), idx.reshape(-1, G, K), synth.to_f64(res).reshape(-1, w.N, w.D)
+    for bh in _sample_heads(w):
+        q, k, v = (_f64_head(d["x"], t, bh, w) for t in "qkv")
+        groups = sorted({0, G // 2, G - 1}) if G > 2 else list(range(G))
+        for g in groups:
+            members = permf[bh, g * w.C:(g + 1) * w.C]
+            ref = oracle.sparse_attention(q[members], k, v, np.arange(members.size), idxf[bh, g:g + 1], w.C,
+                                          scale, residual=resf[bh, members])
+            assert_output_close(o32[bh, members], ref, f"{name} s={density} head {bh} group {g}")
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_select_sampled_groups(mcs, name):
+    w = synth.WORKLOADS[name]
+    d = _inputs(name)
+    s = w.densities[0]
+    K = accounting.k_from_density(s, w.N)
+    G = accounting.num_groups(w.N, w.C)
+    scale = 1 / math.sqrt(w.D)
+    # raster-order groups (perm = identity) are spatially coherent for the video workloads
+    perm = np.broadcast_to(np.arange(w.N, dtype=np.int32), (w.B, w.H, w.N)).copy()
+    _, lse = mcs.dense_attn(d["dev"]["q"], d["dev"]["k"], d["dev"]["v"], scale, want_lse=True)
+    ws = torch.empty(mcs.select_workspace_bytes(d["dev"]["q"].shape, w.C, K), dtype=torch.uint8,
+                     device=lse.device)
+    got = mcs.select(d["dev"]["q"], d["dev"]["k"], lse, to_dev(perm), w.C, K, scale, workspace=ws)
+    got = got.view(-1, G, K).cpu().numpy()
+    for bh in _sample_heads(w):
+        q, k = _f64_head(d["x"], "q", bh, w), _f64_head(d["x"], "k", bh, w)
+        groups = sorted({0, G // 3, G - 1}) if G > 2 else list(range(G))
+        for g in groups:
+            members = np.arange(g * w.C, min((g + 1) * w.C, w.N))
+            _, lse_g = oracle.dense_attention(q[members], k, k, scale)   # only the LSE is used
+            mass = oracle.probabilities(q[members], k, lse_g, scale).sum(axis=0)[None]
+            ref = oracle.topk_indices(mass[0], K)[None]
+            assert_index_sets_match(got[bh, g:g + 1], ref, mass, K, f"{name} head {bh} group {g}")
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_group_full_size(mcs, name):
+    w = synth.WORKLOADS[name]
+    d = _inputs(name)
+    perm = mcs.group(d["dev"]["q"], w.C).cpu().numpy()
+    assert_perm(perm)
+    permf = perm.reshape(-1, w.N)
+    for bh in _sample_heads(w):
+        q = _f64_head(d["x"], "q", bh, w)
+        ref = oracle.pddp(q, w.C)
+        w_ref = oracle.within_group_variance(q, ref, w.C)
+        w_gpu = within_group_variance(q, permf[bh], w.C)
+        assert abs(w_gpu - w_ref) <= 0.01 * w_ref, (name, bh, w_gpu, w_ref)
+
+
+def test_tiny_anchor_and_reuse_in_full(mcs):
+    """Every stage of the tiny workload in full, each fed the oracle's upstream."""
+    w = synth.WORKLOADS["tiny"]
+    d = _inputs("tiny")
+    K = accounting.k_from_density(w.densities[0], w.N)
+    scale = 1 / math.sqrt(w.D)
+    qf, kf, vf = (synth.to_f64(d["x"][t]) for t in "qkv")
+    ref_perm = oracle.pddp_bh(qf, w.C).astype(np.int32)
+    ref_dense, ref_lse = oracle.dense_attention_bh(qf, kf, vf, scale)
+    ref_idx, ref_mass = oracle.select_bh(qf, kf, ref_lse, ref_perm, w.C, K, scale)
+    ref_sp = oracle.sparse_attention_bh(qf, kf, vf, ref_perm, ref_idx, w.C, scale)
+    dq, dk, dv = d["dev"]["q"], d["dev"]["k"], d["dev"]["v"]
+    o_dense, lse = mcs.dense_attn(dq, dk, dv, scale, want_lse=True, out_dtype=torch.float32)
+    assert_output_close(o_dense.cpu().numpy(), ref_dense, "tiny dense")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=0)
+    idx = mcs.select(dq, dk, lse, to_dev(ref_perm), w.C, K, scale).cpu().numpy()
+    for h in range(w.H):
+        assert_index_sets_match(idx[0, h], ref_idx[0, h], ref_mass[0, h], K, f"tiny head {h}")
+    didx = to_dev(ref_idx.astype(np.int32))
+    o_sp = mcs.sparse_attn(dq, dk, dv, to_dev(ref_perm), didx, w.C, scale=scale, out_dtype=torch.float32)
+    assert_output_close(o_sp.cpu().numpy(), ref_sp, "tiny sparse")
+    # reuse step on drifted inputs, with the oracle's anchor residual in bf16
+    x1 = synth.drift("tiny", d["x"], step=1)
+    res_bits = synth.to_bf16_bits((ref_dense - ref_sp).astype(np.float32))
+    o1 = mcs.sparse_attn(*(to_dev_bf16(x1[t]) for t in "qkv"), to_dev(ref_perm), didx, w.C,
+                         residual=to_dev_bf16(res_bits), scale=scale, out_dtype=torch.float32)
+    ref1 = oracle.sparse_attention_bh(*(synth.to_f64(x1[t]) for t in "qkv"), ref_perm, ref_idx, w.C, scale,
+                                      residual=synth.to_f64(res_bits))
+    assert_output_close(o1.cpu().numpy(), ref1, "tiny reuse")
+    perm = mcs.group(dq, w.C).cpu().numpy()
+    assert_perm(perm)
+    for h in range(w.H):
+        w_ref = oracle.within_group_variance(qf[0, h], ref_perm[0, h], w.C)
+        assert abs(within_group_variance(qf[0, h], perm[0, h], w.C) - w_ref) <= 0.01 * w_ref

@@ -1,0 +1,240 @@
+"""Thin ctypes binding of libmcs (include/mcs.h) for torch tensors.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmcs.so.  PyTorch provides device memory and the current HIP stream.  If the
+library has not been built, importing this module raises.
+
+Tensor conventions: q, k, v, outputs and residuals are bf16 [B, H, N, D]
+contiguous device tensors; perm int32 [B, H, N]; kv_idx int32 [B, H, G, K]
+with G = ceil(N / C); lse float32 [B, H, N].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MCS_LIB", os.path.join(_HERE, "libmcs.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libmcs.so not found at {LIB_PATH}: build it with "
+        "`python -m token_sparse_attention_amd.build` (there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+
+_SIGS = {
+    "mcs_dense_attn": ([_P, _P, _P, _P, _P, Dims, _F, _P], _I32),
+    "mcs_sparse_attn": ([_P, _P, _P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P], _I32),
+    "mcs_dense_attn_f32out": ([_P, _P, _P, _P, _P, Dims, _F, _P], _I32),
+    "mcs_sparse_attn_f32out": ([_P, _P, _P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P], _I32),
+    "mcs_residual_update": ([_P, _P, _P, _I64, _P], _I32),
+    "mcs_select": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
+    "mcs_select_workspace": ([Dims, _I32, _I32], _SZ),
+    "mcs_select_workspace_all_heads": ([Dims, _I32, _I32], _SZ),
+    "mcs_topk": ([_P, _P, _I64, _I32, _I32, _P], _I32),
+    "mcs_group": ([_P, _P, Dims, _I32, _I32, _P, _SZ, _P], _I32),
+    "mcs_group_workspace": ([Dims, _I32], _SZ),
+    "mcs_status_string": ([_I32], ctypes.c_char_p),
+    "mcs_last_error": ([], ctypes.c_char_p),
+    "mcs_version": ([], _I32),
+}
+for _name, (_args, _ret) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+
+class McsError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_lib.mcs_status_string(status).decode()} ({status}): {detail}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise McsError(status, _lib.mcs_last_error().decode())
+
+
+def version() -> int:
+    return _lib.mcs_version()
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def dims_of(q: torch.Tensor) -> Dims:
+    B, H, N, D = q.shape
+    return Dims(B, H, N, D)
+
+
+def num_groups(N: int, C: int) -> int:
+    return -(-N // C)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def _qkv(q, k, v=None):
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    if k.shape != q.shape:
+        raise ValueError("q and k must have the same shape")
+    if v is not None:
+        _need(v, "v", torch.bfloat16, 4)
+        if v.shape != q.shape:
+            raise ValueError("q and v must have the same shape")
+
+
+def _out(q, out, out_dtype):
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _need(out, "out", out.dtype, 4)
+    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be bf16 or float32 with the shape of q")
+    return out
+
+
+def dense_attn(q, k, v, scale=None, want_lse=False, out=None, lse=None, out_dtype=torch.bfloat16):
+    """mcs_dense_attn(_f32out): softmax(scale q k^T) v per head, optionally the row LSE.
+
+    The output is bf16 unless out (or out_dtype) is float32."""
+    _qkv(q, k, v)
+    B, H, N, D = q.shape
+    scale = default_scale(D) if scale is None else scale
+    out = _out(q, out, out_dtype)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = _lib.mcs_dense_attn_f32out if out.dtype == torch.float32 else _lib.mcs_dense_attn
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if want_lse else None), dims_of(q), scale,
+              _stream(q)))
+    return (out, lse) if want_lse else out
+
+
+def sparse_attn(q, k, v, perm, kv_idx, C, residual=None, scale=None, out=None, out_dtype=torch.bfloat16):
+    """mcs_sparse_attn(_f32out): each group of C queries attends to its K gathered keys (+ residual).
+
+    The output is bf16 unless out (or out_dtype) is float32."""
+    _qkv(q, k, v)
+    B, H, N, D = q.shape
+    _need(perm, "perm", torch.int32, 3)
+    _need(kv_idx, "kv_idx", torch.int32, 4)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, 4)
+    G = num_groups(N, C)
+    if tuple(kv_idx.shape[:3]) != (B, H, G):
+        raise ValueError(f"kv_idx must be [B, H, G={G}, K] (got {tuple(kv_idx.shape)})")
+    K = kv_idx.shape[3]
+    scale = default_scale(D) if scale is None else scale
+    out = _out(q, out, out_dtype)
+    fn = _lib.mcs_sparse_attn_f32out if out.dtype == torch.float32 else _lib.mcs_sparse_attn
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(kv_idx), _ptr(residual), _ptr(out), dims_of(q),
+              C, K, scale, _stream(q)))
+    return out
+
+
+def residual_update(o_dense, o_sparse, out=None):
+    """mcs_residual_update: bf16(o_dense - o_sparse)."""
+    _need(o_dense, "o_dense", torch.bfloat16, o_dense.dim())
+    _need(o_sparse, "o_sparse", torch.bfloat16, o_sparse.dim())
+    out = torch.empty_like(o_dense) if out is None else out
+    _check(_lib.mcs_residual_update(_ptr(o_dense), _ptr(o_sparse), _ptr(out), o_dense.numel(),
+                                    _stream(o_dense)))
+    return out
+
+
+def select_workspace_bytes(q_shape, C, K, all_heads=True) -> int:
+    d = Dims(*q_shape)
+    fn = _lib.mcs_select_workspace_all_heads if all_heads else _lib.mcs_select_workspace
+    return int(fn(d, C, K))
+
+
+def select(q, k, lse, perm, C, K, scale=None, out=None, workspace=None, max_workspace_bytes=2 << 30):
+    """mcs_select: exact per-group top-K KV ids from recovered probabilities."""
+    _qkv(q, k)
+    B, H, N, D = q.shape
+    _need(lse, "lse", torch.float32, 3)
+    _need(perm, "perm", torch.int32, 3)
+    scale = default_scale(D) if scale is None else scale
+    G = num_groups(N, C)
+    out = torch.empty((B, H, G, K), dtype=torch.int32, device=q.device) if out is None else out
+    if workspace is None:
+        per_head = select_workspace_bytes(q.shape, C, K, all_heads=False)
+        nbytes = min(select_workspace_bytes(q.shape, C, K), max(per_head, max_workspace_bytes // per_head * per_head))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(_lib.mcs_select(_ptr(q), _ptr(k), _ptr(lse), _ptr(perm), _ptr(out), dims_of(q), C, K, scale,
+                           _ptr(workspace), workspace.numel(), _stream(q)))
+    return out
+
+
+def topk(scores, K, out=None):
+    """mcs_topk on float32 [rows, n] non-negative scores -> int32 [rows, K] ascending ids."""
+    _need(scores, "scores", torch.float32, 2)
+    rows, n = scores.shape
+    out = torch.empty((rows, K), dtype=torch.int32, device=scores.device) if out is None else out
+    _check(_lib.mcs_topk(_ptr(scores), _ptr(out), rows, n, K, _stream(scores)))
+    return out
+
+
+def group_workspace_bytes(q_shape, C) -> int:
+    return int(_lib.mcs_group_workspace(Dims(*q_shape), C))
+
+
+def group(q, C, power_iters=0, out=None, workspace=None):
+    """mcs_group: median-split PDDP -> perm int32 [B, H, N]."""
+    _need(q, "q", torch.bfloat16, 4)
+    B, H, N, D = q.shape
+    out = torch.empty((B, H, N), dtype=torch.int32, device=q.device) if out is None else out
+    if workspace is None:
+        workspace = torch.empty(max(group_workspace_bytes(q.shape, C), 16), dtype=torch.uint8, device=q.device)
+    _check(_lib.mcs_group(_ptr(q), _ptr(out), dims_of(q), C, power_iters, _ptr(workspace),
+                          workspace.numel(), _stream(q)))
+    return out
+
+
+def anchor_step(q, k, v, C, K, scale=None, power_iters=0):
+    """Anchor step: group, dense + LSE, select, sparse, residual.  Output is the dense output."""
+    perm = group(q, C, power_iters)
+    o_dense, lse = dense_attn(q, k, v, scale, want_lse=True)
+    kv_idx = select(q, k, lse, perm, C, K, scale)
+    o_sparse = sparse_attn(q, k, v, perm, kv_idx, C, scale=scale)
+    res = residual_update(o_dense, o_sparse)
+    return {"out": o_dense, "perm": perm, "lse": lse, "kv_idx": kv_idx, "o_sparse": o_sparse, "residual": res}
+
+
+def reuse_step(q, k, v, perm, kv_idx, residual, C, scale=None, out=None):
+    """Reuse step: sparse attention with the cached groups, ids and residual."""
+    return sparse_attn(q, k, v, perm, kv_idx, C, residual=residual, scale=scale, out=out)

@@ -1,0 +1,92 @@
+// Device-side building blocks shared by the gfx950 kernels of libmcs.
+//
+// Wave64 everywhere.  Matrix products use the CDNA4 bf16 MFMA
+// v_mfma_f32_32x32x16_bf16: per lane an A fragment (8 bf16 of one row m = lane%32),
+// a B fragment (8 bf16 of one column n = lane%32) and 16 fp32 accumulators.
+// The kernels only rely on two facts about its lane layout:
+//   * A and B use the same k-slot assignment (lane half lane/32, element e), so
+//     whatever k each (half, e) slot stands for, loading A and B with the same
+//     slot -> index mapping computes the intended contraction;
+//   * accumulator element 4*j + i of lane L holds D[8*j + 4*(L/32) + i][L%32].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mcs {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ u32x4_t ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) {
+  return __builtin_bit_cast(bf16x8_t, x);
+}
+
+__device__ __forceinline__ u32x4_t zero_u32x4() {
+  u32x4_t z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the transcendental unit (v_log_f32).
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Values of lanes L and L^32 combined; every lane receives the pair
+// (own, partner) in some order, so max and sum below are symmetric.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // IEEE addition is commutative, so both lanes of a pair get the same sum.
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int clamp_id(int v, int n) { return v < 0 ? 0 : (v >= n ? n - 1 : v); }
+
+// Workgroup -> (head, group) order.  Workgroups are dispatched round-robin over
+// the 8 XCDs; this remap hands every XCD one contiguous range of the logical
+// (head, group) sequence, so the workgroups resident on one XCD work on
+// neighbouring groups of the same head and share its L2.
+__device__ __forceinline__ int xcd_remap(int block, int total) {
+  const int nx = 8;
+  const int xcd = block % nx;
+  const int slot = block / nx;
+  const int base = total / nx, extra = total % nx;
+  return xcd * base + (xcd < extra ? xcd : extra) + slot;
+}
+
+}  // namespace mcs

@@ -29,6 +29,8 @@ Between steps every tensor drifts: X <- bf16(X + sigma * N(0,1)).
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -161,7 +163,9 @@ def generate(name: str, heads=None):
     shape = (1, len(pairs)) if heads is not None else (w.B, w.H)
     out = {t: np.empty(shape + (w.N, w.D), dtype=np.uint16) for t in ("q", "k", "v")}
     pos = _grid_positions(w.grid) if w.kind == "video" else None
-    for i, (b, h) in enumerate(pairs):
+
+    def one(i: int) -> None:
+        b, h = pairs[i]
         if w.kind == "tiny":
             q, k, v = _tiny_head(w.cfg_id, b, h, w.N, w.D)
         elif w.kind == "video":
@@ -172,7 +176,20 @@ def generate(name: str, heads=None):
         out["q"][bi, hi] = to_bf16_bits(q)
         out["k"][bi, hi] = to_bf16_bits(k)
         out["v"][bi, hi] = to_bf16_bits(v)
+
+    _map_heads(one, len(pairs))
     return out
+
+
+def _map_heads(fn, n: int) -> None:
+    """Runs fn(i) for i < n; heads are independent, so a few threads share them."""
+    workers = min(n, max(1, min(16, (os.cpu_count() or 1))))
+    if workers == 1:
+        for i in range(n):
+            fn(i)
+        return
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fn, range(n)))
 
 
 def drift(name: str, tensors: dict, step: int, heads=None) -> dict:
@@ -184,10 +201,14 @@ def drift(name: str, tensors: dict, step: int, heads=None) -> dict:
         x = tensors[t]
         y = np.empty_like(x)
         nh = x.shape[1]
-        for i, (b, h) in enumerate(pairs):
+
+        def one(i: int, x=x, y=y, tid=tid, nh=nh) -> None:
+            b, h = pairs[i]
             bi, hi = divmod(i, nh)
             noise = _rng(w.cfg_id, tid, step, b, h).standard_normal(x.shape[2:], dtype=np.float32)
             y[bi, hi] = to_bf16_bits(to_f32(x[bi, hi]) + np.float32(w.drift) * noise)
+
+        _map_heads(one, len(pairs))
         out[t] = y
     return out
 
@@ -197,9 +218,18 @@ def drift(name: str, tensors: dict, step: int, heads=None) -> dict:
 # ---------------------------------------------------------------------------
 
 def gaussian(shape, seed: int, scale: float = 1.0, mean: float = 0.0) -> np.ndarray:
-    """bf16 bits of mean + scale * N(0,1)."""
-    x = mean + scale * _rng(9000, seed).standard_normal(shape, dtype=np.float32)
-    return to_bf16_bits(x.astype(np.float32))
+    """bf16 bits of mean + scale * N(0,1), drawn in independent chunks of 2^20 values."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    chunk = 1 << 20
+
+    def one(i: int) -> None:
+        lo, hi = i * chunk, min(n, (i + 1) * chunk)
+        x = _rng(9000, seed, i).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = to_bf16_bits(np.float32(mean) + np.float32(scale) * x)
+
+    _map_heads(one, -(-n // chunk))
+    return out.reshape(shape)
 
 
 def random_perm(B: int, H: int, N: int, seed: int) -> np.ndarray:
@@ -218,6 +248,24 @@ def random_index_sets(B: int, H: int, G: int, K: int, N: int, seed: int,
     if ascending:
         sub = np.sort(sub, axis=-1)
     return sub.astype(np.int32)
+
+
+def stratified_index_sets(B: int, H: int, G: int, K: int, N: int, seed: int) -> np.ndarray:
+    """Per (b, h, g) one uniform id in each of K equal strata of 0..N-1 (ascending,
+    distinct): int32 [B, H, G, K]; cheap at full workload sizes."""
+    lo = ((np.arange(K, dtype=np.int64) * N) // K).astype(np.int32)
+    width = (((np.arange(1, K + 1, dtype=np.int64) * N) // K) - lo).astype(np.int32)
+    widthf = width.astype(np.float32)
+    out = np.empty((B * H, G, K), dtype=np.int32)
+
+    def one(i: int) -> None:
+        u = _rng(9400, seed, i).random((G, K), dtype=np.float32)
+        off = (u * widthf).astype(np.int32)
+        np.minimum(off, width - 1, out=off)
+        out[i] = off + lo
+
+    _map_heads(one, B * H)
+    return out.reshape(B, H, G, K)
 
 
 def mass_rows(rows: int, N: int, seed: int, ties: bool = True) -> np.ndarray:
