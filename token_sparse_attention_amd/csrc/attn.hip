@@ -8,25 +8,39 @@
 // selection of individually gathered KV tokens, so the group fills one query
 // tile) with the dense kernel as the same engine on contiguous rows.
 //
-// Tile engine (per workgroup, C/32 waves, each wave owns 32 queries):
+// Tile engine (per workgroup, C/32 waves, each wave owns 32 queries; two
+// workgroups per CU, so two waves share each SIMD and one's softmax overlaps
+// the other's MFMA work):
 //   * Q of the wave's 32 queries stays in registers as MFMA B fragments.
-//   * KV tiles of 64 keys stream through LDS, double buffered: K row-major
-//     (16-byte chunks XOR-swizzled by row) and V transposed to [D][64]
-//     (keys permuted inside each 16-key block so that the 8 keys one lane
-//     needs for a PV step are contiguous).  Gathered rows are 16-byte loads,
-//     16 lanes per 256-byte row, issued one tile ahead of use.
-//   * S^T = K Q^T on MFMA: each lane then holds 32 keys of one query, so the
-//     online softmax is per lane, plus one exchange with lane L^32 for the
-//     running maximum.  Softmax in base 2 with scale*log2(e) folded in.
-//   * O^T += V^T P^T on MFMA, P^T taken straight from the S^T accumulators.
-//   * Epilogue: O = O^T / l (+ residual), bf16, scattered to the query rows;
-//     lse = (m + log2 l) * ln 2 for the dense pass.
+//   * KV tiles of 64 keys are gathered straight into LDS by LDS-DMA
+//     (global_load_lds_dwordx4: each lane moves one 16-byte chunk of a K or V
+//     row, so rows are fetched by id with no staging registers), double
+//     buffered: tile t+1 is in flight while tile t is computed.  K and V are
+//     row-major with 16-byte chunks XOR-swizzled by row; the lane -> chunk
+//     assignment of the DMA realises the swizzle.
+//   * S^T = K Q^T on MFMA (v_mfma_f32_32x32x16_bf16): each lane then holds 32
+//     keys of one query, so the online softmax is per lane plus one exchange
+//     with lane L^32 for the running maximum.  Base-2 softmax with
+//     scale*log2(e) folded into one FMA per score.  The running maximum is
+//     only moved (and O rescaled) when a new score exceeds it by more than
+//     2^8, so most tiles skip the rescale; P stays <= 256, exact in bf16
+//     range, and the final division by the row sum cancels the offset.
+//   * O^T += V^T P^T on MFMA, P^T taken straight from the S^T accumulators and
+//     V^T fragments read with the LDS transpose load ds_read_b64_tr_b16.
+//   * Epilogue: O = O^T / l (+ residual), bf16 or fp32, scattered to the query
+//     rows; lse = (m + log2 l) * ln 2 for the dense pass.
 #include "mcs_common.h"
 #include "mcs_internal.h"
 
 namespace mcs {
 
-constexpr int KT = 64;  // keys per KV tile
+constexpr int KT = 64;          // keys per KV tile
+constexpr float kRescaleSlack = 8.f;   // log2 of the largest unscaled P
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) void* gbl_void_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t* lds_bf16x4_ptr;
 
 struct AttnParams {
   const uint16_t* q;
@@ -41,31 +55,37 @@ struct AttnParams {
   float sl2;              // scale * log2(e)
 };
 
-// LDS chunk swizzles (16-byte chunks).
+// 16-byte chunk swizzle of a K/V row in LDS.
 template <int D>
-__device__ __forceinline__ int swz_k(int row) {
+__device__ __forceinline__ int swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-__device__ __forceinline__ int swz_vt(int d) { return (d >> 1) & 7; }
-// Position of key k (0..63) in a transposed V row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+
+// One 16-byte LDS-DMA per lane: the wave writes 1 KiB at lds (wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t)g, (lds_void_t)lds, 16, 0, 0);
 }
 
-template <int D, int NW, bool SPARSE, bool RES, bool LSE, bool OUTF32>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int CH = D / 8;               // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;          // MFMA k-steps of QK^T
-  constexpr int DB = D / 32;              // 32-row blocks of O^T
-  constexpr int PAIRS = (KT / 4) * CH;    // (4-key quad, chunk) load units per tile
-  constexpr int LIT = (PAIRS + NT - 1) / NT;
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-  __shared__ u32x4_t lds_k[2][KT * CH];
-  __shared__ u32x4_t lds_vt[2][D * (KT / 8)];
+template <int D, int NW, bool SPARSE, bool RES, bool LSE, bool OUTF32>
+__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int KSTEPS = D / 16;            // MFMA k-steps of QK^T
+  constexpr int DB = D / 32;                // 32-row blocks of O^T
+  constexpr int TILE_BYTES = KT * D * 2;    // one K (or V) tile
+  constexpr int INSTR = TILE_BYTES / 1024;  // 1 KiB DMA instructions per K tile
+  constexpr int IPW = INSTR / NW;           // ... per wave
+  constexpr int ROWS_PER_INSTR = 64 / CH;
+  static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+
+  // [stage][K | V][KT * D] bf16
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][KT * D];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int total = p.BH * p.G;
   const int lb = xcd_remap(blockIdx.x, total);
@@ -89,59 +109,29 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   const int ntiles = (nkeys + KT - 1) / KT;
   const int32_t* __restrict__ ids = SPARSE ? p.kv_idx + ((size_t)bh * p.G + g) * p.K : nullptr;
 
-  // ---- KV tile loader: thread -> (quad of 4 consecutive keys, 16-byte chunk) ----
-  u32x4_t kreg[LIT][4], vreg[LIT][4];
-  auto load_tile = [&](int tile) {
+  // ---- DMA plan: instruction j of this wave covers tile rows
+  //      (w*IPW + j)*ROWS_PER_INSTR + lane/CH, one 16-byte chunk per lane ----
+  const int lrow = lane / CH;
+  const int pchunk = lane % CH;
+  int rowid[IPW];        // kv row of each DMA instruction for the next tile to load
+  auto fetch_ids = [&](int tile) {
 #pragma unroll
-    for (int it = 0; it < LIT; ++it) {
-      const int pp = tid + it * NT;
-      if (PAIRS % NT != 0 && pp >= PAIRS) continue;
-      const int quad = pp / CH, chunk = pp - (pp / CH) * CH;
-      const int key0 = tile * KT + quad * 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kp = key0 + r;
-        if (kp < nkeys) {
-          const int row = SPARSE ? clamp_id(ids[kp], p.N) : kp;
-          kreg[it][r] = ldg16(kh + (size_t)row * D + chunk * 8);
-          vreg[it][r] = ldg16(vh + (size_t)row * D + chunk * 8);
-        } else {
-          kreg[it][r] = zero_u32x4();
-          vreg[it][r] = zero_u32x4();
-        }
-      }
+    for (int j = 0; j < IPW; ++j) {
+      int kp = tile * KT + (w * IPW + j) * ROWS_PER_INSTR + lrow;
+      kp = kp < nkeys ? kp : nkeys - 1;   // rows past the end: a valid row, masked later
+      rowid[j] = SPARSE ? clamp_id(ids[kp], p.N) : kp;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto issue_dma = [&](int stage) {
 #pragma unroll
-    for (int it = 0; it < LIT; ++it) {
-      const int pp = tid + it * NT;
-      if (PAIRS % NT != 0 && pp >= PAIRS) continue;
-      const int quad = pp / CH, chunk = pp - (pp / CH) * CH;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = quad * 4 + r;
-        lds_k[buf][row * CH + (chunk ^ swz_k<D>(row))] = kreg[it][r];
-      }
-      const int kpos = vt_pos(quad * 4);
-      u32x2_t* vt2 = reinterpret_cast<u32x2_t*>(&lds_vt[buf][0]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = chunk * 8 + e;
-        const int word = e >> 1;
-        uint32_t a0 = vreg[it][0][word], a1 = vreg[it][1][word];
-        uint32_t a2 = vreg[it][2][word], a3 = vreg[it][3][word];
-        u32x2_t pr;
-        if (e & 1) {
-          pr[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          pr[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-          pr[0] = (a0 & 0xffffu) | (a1 << 16);
-          pr[1] = (a2 & 0xffffu) | (a3 << 16);
-        }
-        const int c = kpos >> 3;
-        vt2[(d * (KT / 8) + (c ^ swz_vt(d))) * 2 + ((kpos >> 2) & 1)] = pr;
-      }
+    for (int j = 0; j < IPW; ++j) {
+      const int r = (w * IPW + j) * ROWS_PER_INSTR + lrow;
+      const int c = pchunk ^ swz<D>(r);   // logical chunk stored at physical chunk pchunk
+      const size_t goff = (size_t)rowid[j] * D + c * 8;
+      char* kdst = reinterpret_cast<char*>(&lds[stage][0][0]) + (w * IPW + j) * 1024;
+      char* vdst = reinterpret_cast<char*>(&lds[stage][1][0]) + (w * IPW + j) * 1024;
+      dma16(kh + goff, kdst);
+      dma16(vh + goff, vdst);
     }
   };
 
@@ -150,13 +140,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = zero16();
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  fetch_ids(0);
+  issue_dma(0);
+  if (ntiles > 1) fetch_ids(1);
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    const int st = t & 1;
+    wait_vmem_all();
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      issue_dma(st ^ 1);
+      if (t + 2 < ntiles) fetch_ids(t + 2);
+    }
+    const uint16_t* kt = &lds[st][0][0];
+    const uint16_t* vt = &lds[st][1][0];
 
     // S^T = K Q^T for the two 32-key blocks of the tile
     f32x16_t sacc[2];
@@ -166,7 +163,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
       const int row = kb * 32 + lq;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t a = as_bf16x8(lds_k[buf][row * CH + ((2 * ks + hh) ^ swz_k<D>(row))]);
+        const bf16x8_t a = as_bf16x8(
+            *reinterpret_cast<const u32x4_t*>(kt + row * D + ((2 * ks + hh) ^ swz<D>(row)) * 8));
         sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
       }
     }
@@ -186,45 +184,53 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * p.sl2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    mx = halves_max(mx) * p.sl2;
+    // move the reference maximum only when a score exceeds it by > 2^slack
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[b][e] *= alpha;
+    }
+    const float mneg = -m_run;
 
     bf16x8_t pf[KT / 16];
-    float lsum = 0.f;
 #pragma unroll
     for (int s = 0; s < KT / 16; ++s) {
       const int kb = s >> 1, e0 = 8 * (s & 1);
       u32x4_t pw;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        const float x0 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd], p.sl2, -m_new));
-        const float x1 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd + 1], p.sl2, -m_new));
-        lsum += x0 + x1;
+        const float x0 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd], p.sl2, mneg));
+        const float x1 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd + 1], p.sl2, mneg));
+        l_run += x0 + x1;
         pw[wd] = pack_bf16x2(x0, x1);
       }
       pf[s] = as_bf16x8(pw);
     }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[b][e] *= alpha;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; V^T fragments by LDS transpose reads: lane group
+    // (lane/16) reads 4 consecutive key rows, lane i%16 gets column i
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const int d = b * 32 + lq;
+      const int dcol = b * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const int rsub = (lane & 15) >> 2;
 #pragma unroll
       for (int s = 0; s < KT / 16; ++s) {
-        const bf16x8_t a = as_bf16x8(lds_vt[buf][d * (KT / 8) + ((2 * s + hh) ^ swz_vt(d))]);
+        const int r0 = 16 * s + 4 * hh + rsub;       // slots e = 0..3
+        const int r1 = r0 + 8;                       // slots e = 4..7
+        const uint16_t* a0p = vt + r0 * D + (((dcol >> 3) ^ swz<D>(r0)) << 3) + (dcol & 7);
+        const uint16_t* a1p = vt + r1 * D + (((dcol >> 3) ^ swz<D>(r1)) << 3) + (dcol & 7);
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a0p));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a1p));
+        const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[b] = mfma32x32x16(a, pf[s], oacc[b]);
       }
     }
-
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue ----
