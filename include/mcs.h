@@ -38,9 +38,11 @@
  *     failed check returns a non-zero status, enqueues nothing, and
  *     mcs_last_error() describes it.  A failed kernel launch returns
  *     MCS_E_HIP.  Device faults surface at the caller's next synchronisation.
- *   - Out-of-range ids in perm or kv_idx are clamped into [0, N) before use,
- *     so they cannot cause out-of-bounds accesses; the result for such input
- *     is unspecified.  NaN/Inf inputs propagate and are not checked.
+ *   - Out-of-range ids cannot cause out-of-bounds accesses: perm entries are
+ *     clamped into [0, N), and a kv_idx entry outside [0, N) reads as a zero
+ *     key and value row; the result for such input is unspecified.  NaN/Inf
+ *     inputs propagate and are not checked.
+ *   - One head's K (N * D * 2 bytes) must stay below 2^31 bytes.
  */
 #ifndef MCS_H
 #define MCS_H

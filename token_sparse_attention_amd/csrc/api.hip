@@ -48,6 +48,8 @@ mcs_status check_dims(const char* fn, mcs_dims d) {
   if (bh > 65535) return fail(MCS_E_SHAPE, "%s: B*H = %lld exceeds 65535", fn, (long long)bh);
   if (bh * d.N > INT32_MAX)
     return fail(MCS_E_SHAPE, "%s: B*H*N = %lld exceeds 2^31-1", fn, (long long)(bh * d.N));
+  if ((int64_t)d.N * d.D * 2 > INT32_MAX)
+    return fail(MCS_E_SHAPE, "%s: one head's K (N*D*2 bytes) exceeds 2^31-1", fn);
   return MCS_OK;
 }
 

@@ -12,12 +12,15 @@
 // workgroups per CU, so two waves share each SIMD and one's softmax overlaps
 // the other's MFMA work):
 //   * Q of the wave's 32 queries stays in registers as MFMA B fragments.
-//   * KV tiles of 64 keys are gathered straight into LDS by LDS-DMA
-//     (global_load_lds_dwordx4: each lane moves one 16-byte chunk of a K or V
-//     row, so rows are fetched by id with no staging registers), double
-//     buffered: tile t+1 is in flight while tile t is computed.  K and V are
-//     row-major with 16-byte chunks XOR-swizzled by row; the lane -> chunk
-//     assignment of the DMA realises the swizzle.
+//   * KV tiles of 64 keys are gathered straight into LDS by buffer loads
+//     with the LDS destination (buffer_load_dwordx4 ... lds: each lane moves
+//     one 16-byte chunk of a K or V row, so rows are fetched by id with no
+//     staging registers; a per-head buffer descriptor bounds the reads and
+//     returns zeros past the end), double buffered: tile t+1 is in flight
+//     while tile t is computed.  K and V are row-major with 16-byte chunks
+//     XOR-swizzled by row; the lane -> chunk assignment of the DMA realises
+//     the swizzle.  All LDS read addresses are per-lane constants plus
+//     immediates (the tile loop is unrolled by the two buffers).
 //   * S^T = K Q^T on MFMA (v_mfma_f32_32x32x16_bf16): each lane then holds 32
 //     keys of one query, so the online softmax is per lane plus one exchange
 //     with lane L^32 for the running maximum.  Base-2 softmax with
@@ -29,6 +32,8 @@
 //     V^T fragments read with the LDS transpose load ds_read_b64_tr_b16.
 //   * Epilogue: O = O^T / l (+ residual), bf16 or fp32, scattered to the query
 //     rows; lse = (m + log2 l) * ln 2 for the dense pass.
+#include <type_traits>
+
 #include "mcs_common.h"
 #include "mcs_internal.h"
 
@@ -38,7 +43,6 @@ constexpr int KT = 64;          // keys per KV tile
 constexpr float kRescaleSlack = 8.f;   // log2 of the largest unscaled P
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
-typedef __attribute__((address_space(1))) void* gbl_void_t;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t* lds_bf16x4_ptr;
 
@@ -55,33 +59,56 @@ struct AttnParams {
   float sl2;              // scale * log2(e)
 };
 
-// 16-byte chunk swizzle of a K/V row in LDS.
+// 16-byte chunk swizzle of a K/V row in LDS (32 banks x 4 bytes: a 16-byte
+// chunk's bank group is its physical chunk index mod 8).  Any 8 consecutive
+// rows get distinct values (conflict-free ds_read_b128 of one logical chunk
+// by 8 lanes), and any 4 rows starting at a multiple of 4 get distinct values
+// of f >> 1 (a transpose read covers 2 adjacent chunks of 4 such rows: all 8
+// land in distinct bank groups).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
-// One 16-byte LDS-DMA per lane: the wave writes 1 KiB at lds (wave-uniform).
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t)g, (lds_void_t)lds, 16, 0, 0);
+// Buffer resource of one head's K or V rows: loads at byte offsets at or past
+// `bytes` return zeros (rows past the end of a tile, ids outside [0, N)).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte buffer load per lane written straight to LDS: the wave writes
+// 1 KiB at lds (wave-uniform) + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)lds, 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 template <int D, int NW, bool SPARSE, bool RES, bool LSE, bool OUTF32>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
-  constexpr int NT = NW * 64;
   constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int ROWB = D * 2;               // bytes per K/V row
   constexpr int KSTEPS = D / 16;            // MFMA k-steps of QK^T
   constexpr int DB = D / 32;                // 32-row blocks of O^T
-  constexpr int TILE_BYTES = KT * D * 2;    // one K (or V) tile
+  constexpr int TILE_BYTES = KT * ROWB;     // one K (or V) tile
+  constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   constexpr int INSTR = TILE_BYTES / 1024;  // 1 KiB DMA instructions per K tile
   constexpr int IPW = INSTR / NW;           // ... per wave
   constexpr int ROWS_PER_INSTR = 64 / CH;
   static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+  static_assert(IPW % 2 == 0 || ROWS_PER_INSTR % 8 == 0, "chunk swizzle period");
 
   // [stage][K | V][KT * D] bf16
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][KT * D];
+  char* const lbase = reinterpret_cast<char*>(&lds[0][0][0]);
+  // sparse: ring of kv ids, two halves of IDS_CHUNK tiles, refilled by DMA
+  // a whole chunk ahead so id latency never reaches the tile loop
+  constexpr int IDS_CHUNK = 32;                       // tiles per ring half
+  constexpr int RING_IDS = SPARSE ? 2 * IDS_CHUNK * KT : 4;
+  __shared__ __attribute__((aligned(1024))) int32_t ring[RING_IDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -92,8 +119,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   const int bh = lb / p.G, g = lb - bh * p.G;
   const size_t head = (size_t)bh * p.N;
   const uint16_t* __restrict__ qh = p.q + head * D;
-  const uint16_t* __restrict__ kh = p.k + head * D;
-  const uint16_t* __restrict__ vh = p.v + head * D;
+  const uint32_t head_bytes = (uint32_t)p.N * ROWB;
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(p.k + head * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v + head * D, head_bytes);
 
   // ---- this lane's query (column lq of the wave's 32-query block) ----
   const int qpos = g * p.C + w * 32 + lq;
@@ -109,62 +137,92 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   const int ntiles = (nkeys + KT - 1) / KT;
   const int32_t* __restrict__ ids = SPARSE ? p.kv_idx + ((size_t)bh * p.G + g) * p.K : nullptr;
 
-  // ---- DMA plan: instruction j of this wave covers tile rows
-  //      (w*IPW + j)*ROWS_PER_INSTR + lane/CH, one 16-byte chunk per lane ----
+  // ---- DMA plan: instruction j of this wave fills tile rows
+  //      (w*IPW + j)*ROWS_PER_INSTR + lane/CH, physical chunk lane%CH ----
   const int lrow = lane / CH;
   const int pchunk = lane % CH;
-  int rowid[IPW];        // kv row of each DMA instruction for the next tile to load
+  uint32_t coff[2];      // byte offset of this lane's logical chunk in its row, by j parity
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int r = (w * IPW + par) * ROWS_PER_INSTR + lrow;
+    coff[par] = (uint32_t)((pchunk ^ swz<D>(r)) * 16);
+  }
+  uint32_t rowoff[IPW];  // byte offset of the kv row of each DMA instruction (next tile to load)
+  // Sparse: ids come from the LDS ring; ring positions past K hold zeros (the
+  // id buffer descriptor ends at K), and those keys are masked after QK^T.
   auto fetch_ids = [&](int tile) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      int kp = tile * KT + (w * IPW + j) * ROWS_PER_INSTR + lrow;
-      kp = kp < nkeys ? kp : nkeys - 1;   // rows past the end: a valid row, masked later
-      rowid[j] = SPARSE ? clamp_id(ids[kp], p.N) : kp;
+      const int r = (w * IPW + j) * ROWS_PER_INSTR + lrow;
+      const int kp = tile * KT + r;
+      int row;
+      if (SPARSE) row = ring[(tile % (2 * IDS_CHUNK)) * KT + r];
+      else row = kp < nkeys ? kp : -1;   // -1: past the end -> zero rows
+      rowoff[j] = (uint32_t)row * (uint32_t)ROWB;
     }
   };
-  auto issue_dma = [&](int stage) {
+  // refill ring half (chunk & 1) with the ids of tiles [chunk*IDS_CHUNK, +IDS_CHUNK)
+  __amdgpu_buffer_rsrc_t rids;
+  if (SPARSE) rids = head_rsrc(ids, (uint32_t)p.K * 4u);
+  auto refill_ids = [&](int chunk) {
+    constexpr int BYTES = IDS_CHUNK * KT * 4;           // 8 KiB per half
+    constexpr int PER_WAVE = BYTES / 1024 / NW;
+    char* half = reinterpret_cast<char*>(&ring[0]) + (chunk & 1) * BYTES;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = w * PER_WAVE + j;                 // 1 KiB block of the half
+      dma16(rids, (uint32_t)(chunk * BYTES + blk * 1024 + lane * 16), half + blk * 1024);
+    }
+  };
+  auto issue_dma = [&](auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      const int r = (w * IPW + j) * ROWS_PER_INSTR + lrow;
-      const int c = pchunk ^ swz<D>(r);   // logical chunk stored at physical chunk pchunk
-      const size_t goff = (size_t)rowid[j] * D + c * 8;
-      char* kdst = reinterpret_cast<char*>(&lds[stage][0][0]) + (w * IPW + j) * 1024;
-      char* vdst = reinterpret_cast<char*>(&lds[stage][1][0]) + (w * IPW + j) * 1024;
-      dma16(kh + goff, kdst);
-      dma16(vh + goff, vdst);
+      const uint32_t voff = rowoff[j] + coff[j & 1];
+      dma16(rk, voff, lbase + ST * STAGE_BYTES + (w * IPW + j) * 1024);
+      dma16(rv, voff, lbase + ST * STAGE_BYTES + TILE_BYTES + (w * IPW + j) * 1024);
     }
   };
+
+  // ---- per-lane LDS read offsets (stage, key block and k-step are immediates) ----
+  uint32_t koff[KSTEPS];   // K fragment of k-step ks, key row lq
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    koff[ks] = (uint32_t)(lq * ROWB + (((2 * ks + hh) ^ swz<D>(lq)) << 4));
+  const int rsub = (lane & 15) >> 2;
+  uint32_t voff_tr[DB];    // transpose read of d-block b, key row 4*hh + rsub
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const int dcol = b * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int r = 4 * hh + rsub;
+    voff_tr[b] = (uint32_t)(r * ROWB + (((dcol >> 3) ^ swz<D>(r)) << 4) + (dcol & 7) * 2);
+  }
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = zero16();
 
-  fetch_ids(0);
-  issue_dma(0);
-  if (ntiles > 1) fetch_ids(1);
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
+  auto tile_step = [&](auto stage_c, int t) {
+    constexpr int ST = decltype(stage_c)::value;
     wait_vmem_all();
     __syncthreads();
+    if (SPARSE && t % IDS_CHUNK == 0 && t + IDS_CHUNK < ntiles) refill_ids(t / IDS_CHUNK + 1);
     if (t + 1 < ntiles) {
-      issue_dma(st ^ 1);
-      if (t + 2 < ntiles) fetch_ids(t + 2);
+      fetch_ids(t + 1);
+      issue_dma(ic<ST ^ 1>{});
     }
-    const uint16_t* kt = &lds[st][0][0];
-    const uint16_t* vt = &lds[st][1][0];
+    const char* kt = lbase + ST * STAGE_BYTES;
+    const char* vt = kt + TILE_BYTES;
 
     // S^T = K Q^T for the two 32-key blocks of the tile
     f32x16_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = zero16();
-      const int row = kb * 32 + lq;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t a = as_bf16x8(
-            *reinterpret_cast<const u32x4_t*>(kt + row * D + ((2 * ks + hh) ^ swz<D>(row)) * 8));
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kt + kb * 32 * ROWB + koff[ks]));
         sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
       }
     }
@@ -217,21 +275,31 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
     // (lane/16) reads 4 consecutive key rows, lane i%16 gets column i
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const int dcol = b * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      const int rsub = (lane & 15) >> 2;
 #pragma unroll
       for (int s = 0; s < KT / 16; ++s) {
-        const int r0 = 16 * s + 4 * hh + rsub;       // slots e = 0..3
-        const int r1 = r0 + 8;                       // slots e = 4..7
-        const uint16_t* a0p = vt + r0 * D + (((dcol >> 3) ^ swz<D>(r0)) << 3) + (dcol & 7);
-        const uint16_t* a1p = vt + r1 * D + (((dcol >> 3) ^ swz<D>(r1)) << 3) + (dcol & 7);
+        const char* a0p = vt + (16 * s) * ROWB + voff_tr[b];       // slots e = 0..3
+        const char* a1p = vt + (16 * s + 8) * ROWB + voff_tr[b];   // slots e = 4..7
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a0p));
         const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a1p));
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[b] = mfma32x32x16(a, pf[s], oacc[b]);
       }
     }
+  };
+
+  if (SPARSE) {
+    refill_ids(0);
+    wait_vmem_all();
+    __syncthreads();
   }
+  fetch_ids(0);
+  issue_dma(ic<0>{});
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    tile_step(ic<0>{}, t);
+    tile_step(ic<1>{}, t + 1);
+  }
+  if (t < ntiles) tile_step(ic<0>{}, t);
 
   // ---- epilogue ----
   const float l_tot = halves_sum(l_run);
