@@ -37,6 +37,11 @@ Readings of points the pages leave open (each listed in the design doc as well):
      with g = ceil(n/C) groups in the node; the exact split is the median when g
      is even and n = g*C; the remainder group ends up rightmost;
   R6 principal direction sign: largest-|.| component positive (ties -> lowest id);
+  R6b the principal direction of a PDDP node comes from power iteration, the
+     pages' algorithm for Fast PDDP (ai.info "Key Contributions": batched power
+     iteration): 32 steps on the node covariance, started from its column of
+     largest diagonal, normalised every step (the pages give neither count nor
+     start); mode="eigh" gives the exact eigenvector instead;
   R7 the residual is O_dense - O_sparse formed at the anchor with the anchor's
      own Q, K, V and the freshly built groups and indices.
 
@@ -192,8 +197,8 @@ def residual(o_dense, o_sparse) -> np.ndarray:
     return _f64(o_dense) - _f64(o_sparse)
 
 
-def anchor_step(q, k, v, C: int, K: int, scale: float, pddp_mode: str = "eigh",
-                power_iters: int = 16):
+def anchor_step(q, k, v, C: int, K: int, scale: float, pddp_mode: str = "power",
+                power_iters: int = 32):
     """One anchor step of one head, in the pages' order.
 
     Groups (PDDP), dense attention + LSE (pass 1), group mass + top-K (pass 2),
@@ -261,13 +266,15 @@ def principal_direction(x, mode: str = "eigh", power_iters: int = 16):
     return mu, _canonical_sign(vec)
 
 
-def pddp(q, C: int, mode: str = "eigh", power_iters: int = 16) -> np.ndarray:
+def pddp(q, C: int, mode: str = "power", power_iters: int = 32) -> np.ndarray:
     """Median-split PDDP of one head's queries into exactly-C groups.
 
     Node with ids I (n = |I|, g = ceil(n/C) groups): a leaf when g == 1;
-    otherwise order I by (projection on the principal direction, query id),
-    left child = first C*floor(g/2) ids, right child = the rest (R5).  Leaves
-    are emitted left-first, so perm[g*C:(g+1)*C] is group g.  Returns perm [N].
+    otherwise order I by (projection on the node's principal direction, query
+    id), left child = first C*floor(g/2) ids, right child = the rest (R5).
+    Leaves are emitted left-first, so perm[g*C:(g+1)*C] is group g.  The
+    direction comes from power iteration by default (R6b), or from eigh.
+    Returns perm [N].
     """
     q = _f64(q)
     leaves: list[np.ndarray] = []
@@ -339,7 +346,7 @@ def select_bh(q, k, lse, perm, C: int, K: int, scale: float):
     return idx, mass
 
 
-def pddp_bh(q, C: int, mode: str = "eigh", power_iters: int = 16) -> np.ndarray:
+def pddp_bh(q, C: int, mode: str = "power", power_iters: int = 32) -> np.ndarray:
     qs, bh = _heads(q)
     perms = [pddp(qs[i], C, mode=mode, power_iters=power_iters) for i in range(qs.shape[0])]
     return np.stack(perms).reshape(bh + perms[0].shape)

@@ -91,6 +91,24 @@ def test_refinement_and_variance_monotone():
     assert prev_w < total
 
 
+def test_default_direction_is_power_iteration():
+    # power iteration (the pages' Fast PDDP) is the default; eigh stays available
+    q = _rand((300, 6), 21) * np.array([3.0, 2.9, 1.0, 0.5, 0.3, 0.1])
+    assert np.array_equal(oracle.pddp(q, 16), oracle.pddp(q, 16, mode="power", power_iters=32))
+    for mode in ("eigh", "power"):
+        perm = oracle.pddp(q, 16, mode=mode)
+        assert sorted(perm.tolist()) == list(range(300))
+
+
+def test_power_mode_with_many_steps_matches_eigh_grouping():
+    q = _rand((512, 5), 22) * np.array([5.0, 3.0, 2.0, 1.0, 0.5])
+    a = oracle.pddp(q, 32, mode="eigh")
+    b = oracle.pddp(q, 32, mode="power", power_iters=500)
+    ga = {frozenset(g.tolist()) for g in oracle.groups_from_perm(a, 32)}
+    gb = {frozenset(g.tolist()) for g in oracle.groups_from_perm(b, 32)}
+    assert ga == gb
+
+
 def test_identical_queries_split_by_query_id():
     q = np.ones((40, 4))
     perm = oracle.pddp(q, 8)
