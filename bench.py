@@ -98,6 +98,23 @@ def cpu_baseline(args, w, x, K, scale):
     }
 
 
+def measured_traffic(workload: str, kernel_prefix: str):
+    """HBM bytes per launch from the committed counter summary, if it still
+    describes the current kernel sources (else None)."""
+    from token_sparse_attention_amd import pmc
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != pmc.source_hash():
+        return None
+    for name, v in d["kernels"].items():
+        if name.startswith(kernel_prefix):
+            return v["traffic_bytes"]
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -216,9 +233,15 @@ def main():
                    "step": "anchor (group, dense+lse, select, sparse, residual) + reuse (sparse + residual)",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload, f"attn_kernel<{D}, {w.C // 32}, true, true"),
                      "kernel": "attn_kernel (sparse, residual epilogue)",
-                     "per_launch_flops": sparse_flops, "avg_launch_ms": round(ms["sparse_reuse"], 4)},
+                     "per_launch_flops": sparse_flops, "avg_launch_ms": round(ms["sparse_reuse"], 4),
+                     "algorithmic_bytes": accounting.sparse_compulsory_bytes(B, H, N, K, D, w.C),
+                     "gathered_bytes": accounting.sparse_gather_bytes(B, H, N, K, D, w.C)},
+        "roofline_dense": {"bound": "mfma", "achieved": round(dense_flops / (ms["dense_lse"] * 1e-3) / 1e12, 2),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(dense_flops / (ms["dense_lse"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "stage_ms": {k: round(v, 4) for k, v in ms.items()},
         "dense_nolse_ms": round(dense_nolse_ms, 4),
         "speedup_vs_dense_nolse": round(dense_nolse_ms / ms["sparse_reuse"], 4),

@@ -29,7 +29,10 @@
 //     2^8, so most tiles skip the rescale; P stays <= 256, exact in bf16
 //     range, and the final division by the row sum cancels the offset.
 //   * O^T += V^T P^T on MFMA, P^T taken straight from the S^T accumulators and
-//     V^T fragments read with the LDS transpose load ds_read_b64_tr_b16.
+//     V^T fragments read with the LDS transpose load ds_read_b64_tr_b16.  O
+//     is normalised by the sum of the same bf16-rounded P that enter the
+//     product (v_dot2c_f32_bf16 against (1, 1)), so its error scales with
+//     |v_j - o| instead of |v_j|; the LSE uses the exact fp32 sum.
 //   * Epilogue: O = O^T / l (+ residual), bf16 or fp32, scattered to the query
 //     rows; lse = (m + log2 l) * ln 2 for the dense pass.
 #include <type_traits>
@@ -198,7 +201,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
     voff_tr[b] = (uint32_t)(r * ROWB + (((dcol >> 3) ^ swz<D>(r)) << 4) + (dcol & 7) * 2);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // l_run: row sum of the bf16-rounded P that enter PV (normalises O
+  // consistently: errors then scale with |v_j - o| rather than |v_j|);
+  // l_lse: the exact fp32 row sum, for the LSE output.
+  float m_run = -INFINITY, l_run = 0.f, l_lse = 0.f;
   f32x16_t oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = zero16();
@@ -249,6 +255,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
+      if (LSE) l_lse *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -265,8 +272,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
       for (int wd = 0; wd < 4; ++wd) {
         const float x0 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd], p.sl2, mneg));
         const float x1 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd + 1], p.sl2, mneg));
-        l_run += x0 + x1;
         pw[wd] = pack_bf16x2(x0, x1);
+        l_run = add_bf16_pair(pw[wd], l_run);
+        if (LSE) l_lse += x0 + x1;
       }
       pf[s] = as_bf16x8(pw);
     }
@@ -303,6 +311,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
 
   // ---- epilogue ----
   const float l_tot = halves_sum(l_run);
+  const float l_exact = LSE ? halves_sum(l_lse) : 0.f;
   if (!qvalid) return;
   const float inv = 1.f / l_tot;
   uint16_t* orow = static_cast<uint16_t*>(p.o) + (head + qrow) * D;
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
         *reinterpret_cast<u32x2_t*>(orow + d0) = out;
       }
     }
-  if (LSE && hh == 0) p.lse[head + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+  if (LSE && hh == 0) p.lse[head + qrow] = (m_run + fast_log2(l_exact)) * kLn2;
 }
 
 template <int D, int NW, bool SPARSE, bool RES, bool LSE, bool OUTF32>
