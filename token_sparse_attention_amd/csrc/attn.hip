@@ -43,6 +43,15 @@
 namespace mcs {
 
 constexpr int KT = 64;          // keys per KV tile
+#ifndef MCS_SCHED_LOOKAHEAD
+#define MCS_SCHED_LOOKAHEAD 4        // LDS fragment reads issued ahead of their MFMA
+#endif
+#ifndef MCS_S_ALTERNATE
+#define MCS_S_ALTERNATE 0            // interleave the two S accumulation chains
+#endif
+#ifndef MCS_SCHED_VALU
+#define MCS_SCHED_VALU 4             // VALU instructions interleaved after each S MFMA
+#endif
 constexpr float kRescaleSlack = 8.f;   // log2 of the largest unscaled P
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -62,15 +71,19 @@ struct AttnParams {
   float sl2;              // scale * log2(e)
 };
 
-// 16-byte chunk swizzle of a K/V row in LDS (32 banks x 4 bytes: a 16-byte
-// chunk's bank group is its physical chunk index mod 8).  Any 8 consecutive
-// rows get distinct values (conflict-free ds_read_b128 of one logical chunk
-// by 8 lanes), and any 4 rows starting at a multiple of 4 get distinct values
-// of f >> 1 (a transpose read covers 2 adjacent chunks of 4 such rows: all 8
-// land in distinct bank groups).
+// 16-byte chunk swizzle of a K/V row in LDS.  The gfx950 LDS has 64 banks of
+// 4 bytes, i.e. 16 bank groups of 16 bytes; a ds_read_b128 serves 16 lanes per
+// cycle and a ds_read_b64_tr_b16 32 lanes.  D = 128 (256-byte rows, bank
+// group = physical chunk): f maps any 16 consecutive rows to a permutation of
+// 0..15 (K fragment reads: 16 rows, one logical chunk) and the 4 rows of a
+// transpose read (rows 4a..4a+3) to 0, 4, 8, 12 (+ a constant), so their 4
+// consecutive chunks land in 16 distinct groups.  D = 64 (128-byte rows, two
+// rows per bank row): the same two properties with the row's half taken into
+// account.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  return ((row & 3) << 1) | ((row >> 2) & 1);
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 // Buffer resource of one head's K or V rows: loads at byte offsets at or past
@@ -102,7 +115,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   constexpr int IPW = INSTR / NW;           // ... per wave
   constexpr int ROWS_PER_INSTR = 64 / CH;
   static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
-  static_assert(IPW % 2 == 0 || ROWS_PER_INSTR % 8 == 0, "chunk swizzle period");
 
   // [stage][K | V][KT * D] bf16
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][KT * D];
@@ -144,16 +156,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   //      (w*IPW + j)*ROWS_PER_INSTR + lane/CH, physical chunk lane%CH ----
   const int lrow = lane / CH;
   const int pchunk = lane % CH;
-  uint32_t coff[2];      // byte offset of this lane's logical chunk in its row, by j parity
+  uint32_t coff[IPW];    // byte offset of this lane's logical chunk in its row, per instruction
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int r = (w * IPW + par) * ROWS_PER_INSTR + lrow;
-    coff[par] = (uint32_t)((pchunk ^ swz<D>(r)) * 16);
+  for (int j = 0; j < IPW; ++j) {
+    const int r = (w * IPW + j) * ROWS_PER_INSTR + lrow;
+    coff[j] = (uint32_t)((pchunk ^ swz<D>(r)) * 16);
   }
-  uint32_t rowoff[IPW];  // byte offset of the kv row of each DMA instruction (next tile to load)
   // Sparse: ids come from the LDS ring; ring positions past K hold zeros (the
   // id buffer descriptor ends at K), and those keys are masked after QK^T.
-  auto fetch_ids = [&](int tile) {
+  auto fetch_ids = [&](int tile, uint32_t (&rowoff)[IPW]) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int r = (w * IPW + j) * ROWS_PER_INSTR + lrow;
@@ -177,29 +188,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
       dma16(rids, (uint32_t)(chunk * BYTES + blk * 1024 + lane * 16), half + blk * 1024);
     }
   };
-  auto issue_dma = [&](auto stage_c) {
-    constexpr int ST = decltype(stage_c)::value;
+  // K tiles live in lds[*][0], V tiles in lds[*][1]; K runs one tile ahead of V
+  auto issue_k = [&](auto buf_c, const uint32_t (&rowoff)[IPW]) {
+    constexpr int BUF = decltype(buf_c)::value;
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const uint32_t voff = rowoff[j] + coff[j & 1];
-      dma16(rk, voff, lbase + ST * STAGE_BYTES + (w * IPW + j) * 1024);
-      dma16(rv, voff, lbase + ST * STAGE_BYTES + TILE_BYTES + (w * IPW + j) * 1024);
-    }
+    for (int j = 0; j < IPW; ++j)
+      dma16(rk, rowoff[j] + coff[j], lbase + BUF * STAGE_BYTES + (w * IPW + j) * 1024);
+  };
+  auto issue_v = [&](auto buf_c, const uint32_t (&rowoff)[IPW]) {
+    constexpr int BUF = decltype(buf_c)::value;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j)
+      dma16(rv, rowoff[j] + coff[j], lbase + BUF * STAGE_BYTES + TILE_BYTES + (w * IPW + j) * 1024);
   };
 
-  // ---- per-lane LDS read offsets (stage, key block and k-step are immediates) ----
+  // ---- per-lane LDS read offsets (buffer, key block and k-step are immediates) ----
   uint32_t koff[KSTEPS];   // K fragment of k-step ks, key row lq
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks)
     koff[ks] = (uint32_t)(lq * ROWB + (((2 * ks + hh) ^ swz<D>(lq)) << 4));
   const int rsub = (lane & 15) >> 2;
-  uint32_t voff_tr[DB];    // transpose read of d-block b, key row 4*hh + rsub
+  // transpose reads of d-block b: key rows 16s + 4*hh + rsub (slots 0..3) and
+  // 16s + 8 + 4*hh + rsub (slots 4..7); the swizzle of a row depends on it
+  // only through row mod 16, so s enters as an immediate
+  uint32_t voff_tr[2][DB];
 #pragma unroll
-  for (int b = 0; b < DB; ++b) {
-    const int dcol = b * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int r = 4 * hh + rsub;
-    voff_tr[b] = (uint32_t)(r * ROWB + (((dcol >> 3) ^ swz<D>(r)) << 4) + (dcol & 7) * 2);
-  }
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const int dcol = b * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const int r = 8 * half + 4 * hh + rsub;
+      voff_tr[half][b] = (uint32_t)(r * ROWB + (((dcol >> 3) ^ swz<D>(r)) << 4) + (dcol & 7) * 2);
+    }
 
   // l_run: row sum of the bf16-rounded P that enter PV (normalises O
   // consistently: errors then scale with |v_j - o| rather than |v_j|);
@@ -209,40 +229,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = zero16();
 
-  auto tile_step = [&](auto stage_c, int t) {
-    constexpr int ST = decltype(stage_c)::value;
-    wait_vmem_all();
-    __syncthreads();
-    if (SPARSE && t % IDS_CHUNK == 0 && t + IDS_CHUNK < ntiles) refill_ids(t / IDS_CHUNK + 1);
-    if (t + 1 < ntiles) {
-      fetch_ids(t + 1);
-      issue_dma(ic<ST ^ 1>{});
-    }
-    const char* kt = lbase + ST * STAGE_BYTES;
-    const char* vt = kt + TILE_BYTES;
-
-    // S^T = K Q^T for the two 32-key blocks of the tile
-    f32x16_t sacc[2];
+  // S^T = K Q^T for the two 32-key blocks of the K tile in buffer BUF
+  auto compute_s = [&](auto buf_c, f32x16_t (&sacc)[2]) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const char* kt = lbase + BUF * STAGE_BYTES;
+    sacc[0] = zero16();
+    sacc[1] = zero16();
+#if MCS_S_ALTERNATE
+    // the two 32-key blocks' accumulation chains alternate
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = zero16();
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kt + kb * 32 * ROWB + koff[ks]));
+        sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
+      }
+#else
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kt + kb * 32 * ROWB + koff[ks]));
         sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
       }
-    }
-    if ((t + 1) * KT > nkeys) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = t * KT + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key >= nkeys) sacc[kb][e] = -INFINITY;
-        }
-    }
+#endif
+  };
 
-    // online softmax (base 2), one query per lane
+  // ---- online softmax of one tile's scores (base 2), one query per lane ----
+  // part 1: row max, and the (rare, wave-uniform) move of the reference max
+  auto softmax_max = [&](f32x16_t (&sacc)[2]) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -261,9 +276,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[b][e] *= alpha;
     }
+  };
+  // part 2: P = exp2(s*scale*log2e - m) as bf16 MFMA fragments, row sums
+  auto softmax_p = [&](f32x16_t (&sacc)[2], bf16x8_t (&pf)[KT / 16]) {
     const float mneg = -m_run;
-
-    bf16x8_t pf[KT / 16];
 #pragma unroll
     for (int s = 0; s < KT / 16; ++s) {
       const int kb = s >> 1, e0 = 8 * (s & 1);
@@ -278,15 +294,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
       }
       pf[s] = as_bf16x8(pw);
     }
-
-    // O^T += V^T P^T; V^T fragments by LDS transpose reads: lane group
-    // (lane/16) reads 4 consecutive key rows, lane i%16 gets column i
+  };
+  // O^T += V^T P^T with the V tile in BUF; V^T fragments by LDS transpose
+  // reads (lane group lane/16 reads 4 consecutive key rows, lane i%16 gets
+  // column i)
+  auto pv = [&](auto buf_c, const bf16x8_t (&pf)[KT / 16]) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const char* vt = lbase + BUF * STAGE_BYTES + TILE_BYTES;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
+    for (int s = 0; s < KT / 16; ++s) {
 #pragma unroll
-      for (int s = 0; s < KT / 16; ++s) {
-        const char* a0p = vt + (16 * s) * ROWB + voff_tr[b];       // slots e = 0..3
-        const char* a1p = vt + (16 * s + 8) * ROWB + voff_tr[b];   // slots e = 4..7
+      for (int b = 0; b < DB; ++b) {
+        const char* a0p = vt + (16 * s) * ROWB + voff_tr[0][b];    // slots e = 0..3
+        const char* a1p = vt + (16 * s) * ROWB + voff_tr[1][b];    // slots e = 4..7
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a0p));
         const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a1p));
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -295,19 +315,100 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
     }
   };
 
+  // Software pipeline.  Iteration t (buffer parity P = t & 1) waits for K_{t+1}
+  // and V_t, issues the gathers of V_{t+1} (into V buffer P^1) and K_{t+2}
+  // (into K buffer P), takes the row max of S_t, then in one branch-free
+  // block computes S_{t+1} = K_{t+1} Q^T on MFMA interleaved with the
+  // exponentials of S_t on the VALU, and O += V_t P_t.  Only the last tile
+  // can be partial; it is peeled off and masked.
+  uint32_t rowk[IPW], rowv[IPW];
+  auto step_head = [&](auto par_c, int t) {
+    constexpr int P = decltype(par_c)::value;
+    wait_vmem_all();
+    __syncthreads();
+    if (SPARSE && t % IDS_CHUNK == 0 && t + IDS_CHUNK < ntiles) refill_ids(t / IDS_CHUNK + 1);
+    if (t + 1 < ntiles) issue_v(ic<P ^ 1>{}, rowv);
+    if (t + 2 < ntiles) {
+      fetch_ids(t + 2, rowk);
+      issue_k(ic<P>{}, rowk);
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
+    }
+  };
+  auto steady_step = [&](auto par_c, int t, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
+    constexpr int P = decltype(par_c)::value;
+    step_head(par_c, t);
+    softmax_max(s_cur);
+    bf16x8_t pf[KT / 16];
+    softmax_p(s_cur, pf);
+    compute_s(ic<P ^ 1>{}, s_nxt);
+    pv(ic<P>{}, pf);
+    // interleave: K fragment reads run LOOKAHEAD MFMAs ahead; each S MFMA is
+    // followed by a share of the exponentials' VALU work; then the PV MFMAs
+    // with their transpose reads, also run ahead
+    constexpr int LOOKAHEAD = MCS_SCHED_LOOKAHEAD;
+    __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);        // DS read
+#pragma unroll
+    for (int i = 0; i < 2 * KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, MCS_SCHED_VALU, 0); // VALU
+      if (i + LOOKAHEAD < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LOOKAHEAD, 0);    // DS read (transpose)
+#pragma unroll
+    for (int i = 0; i < (KT / 16) * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);              // VALU
+      if (i + LOOKAHEAD < (KT / 16) * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+  auto last_step = [&](auto par_c, int t, f32x16_t (&s_cur)[2]) {
+    constexpr int P = decltype(par_c)::value;
+    step_head(par_c, t);
+    if ((t + 1) * KT > nkeys) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = t * KT + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          if (key >= nkeys) s_cur[kb][e] = -INFINITY;
+        }
+    }
+    softmax_max(s_cur);
+    bf16x8_t pf[KT / 16];
+    softmax_p(s_cur, pf);
+    pv(ic<P>{}, pf);
+  };
+
   if (SPARSE) {
     refill_ids(0);
     wait_vmem_all();
     __syncthreads();
   }
-  fetch_ids(0);
-  issue_dma(ic<0>{});
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    tile_step(ic<0>{}, t);
-    tile_step(ic<1>{}, t + 1);
+  fetch_ids(0, rowk);
+  issue_k(ic<0>{}, rowk);
+  issue_v(ic<0>{}, rowk);
+  if (ntiles > 1) {
+    fetch_ids(1, rowk);
+    issue_k(ic<1>{}, rowk);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
   }
-  if (t < ntiles) tile_step(ic<0>{}, t);
+  wait_vmem_all();
+  __syncthreads();
+  f32x16_t sa[2], sb[2];
+  compute_s(ic<0>{}, sa);
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    steady_step(ic<0>{}, t, sa, sb);
+    steady_step(ic<1>{}, t + 1, sb, sa);
+  }
+  if (t + 1 < ntiles) {        // tiles t (full) and t + 1 (last) remain
+    steady_step(ic<0>{}, t, sa, sb);
+    last_step(ic<1>{}, t + 1, sb);
+  } else {                     // tile t is the last
+    last_step(ic<0>{}, t, sa);
+  }
 
   // ---- epilogue ----
   const float l_tot = halves_sum(l_run);

@@ -37,9 +37,12 @@ struct MassParams {
   float sl2;
 };
 
+// 16-byte chunk swizzle of a K row in LDS (64 banks of 4 bytes): 16
+// consecutive rows reading one logical chunk hit 16 distinct bank groups.
 template <int D>
 __device__ __forceinline__ int mswz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 template <int D, int NW>
