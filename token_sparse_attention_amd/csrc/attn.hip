@@ -94,8 +94,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
 
 // One 16-byte buffer load per lane written straight to LDS: the wave writes
 // 1 KiB at lds (wave-uniform) + 16 * lane.
+//
+// Issued as inline assembly on purpose: the compiler cannot tell the LDS
+// range a DMA writes from the ranges the tile loop reads, and for the builtin
+// it places a full vmcnt wait before the next LDS read, which would make every
+// step wait for the gathers it has just issued.  Here the kernel orders DMA
+// and LDS reads itself (an explicit vmcnt wait and a barrier at the head of
+// each step; reads and DMA writes of one step touch disjoint buffers).  VMEM
+// operations the compiler does not see can only make its own (in-order)
+// vmcnt waits stricter, never looser.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)lds, 16, voff, 0, 0, 0);
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_t)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
