@@ -54,7 +54,6 @@ constexpr int KT = 64;          // keys per KV tile
 #endif
 constexpr float kRescaleSlack = 8.f;   // log2 of the largest unscaled P
 
-typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t* lds_bf16x4_ptr;
 
@@ -70,45 +69,6 @@ struct AttnParams {
   int32_t N, C, K, G, BH;
   float sl2;              // scale * log2(e)
 };
-
-// 16-byte chunk swizzle of a K/V row in LDS.  The gfx950 LDS has 64 banks of
-// 4 bytes, i.e. 16 bank groups of 16 bytes; a ds_read_b128 serves 16 lanes per
-// cycle and a ds_read_b64_tr_b16 32 lanes.  D = 128 (256-byte rows, bank
-// group = physical chunk): f maps any 16 consecutive rows to a permutation of
-// 0..15 (K fragment reads: 16 rows, one logical chunk) and the 4 rows of a
-// transpose read (rows 4a..4a+3) to 0, 4, 8, 12 (+ a constant), so their 4
-// consecutive chunks land in 16 distinct groups.  D = 64 (128-byte rows, two
-// rows per bank row): the same two properties with the row's half taken into
-// account.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-// Buffer resource of one head's K or V rows: loads at byte offsets at or past
-// `bytes` return zeros (rows past the end of a tile, ids outside [0, N)).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// One 16-byte buffer load per lane written straight to LDS: the wave writes
-// 1 KiB at lds (wave-uniform) + 16 * lane.
-//
-// Issued as inline assembly on purpose: the compiler cannot tell the LDS
-// range a DMA writes from the ranges the tile loop reads, and for the builtin
-// it places a full vmcnt wait before the next LDS read, which would make every
-// step wait for the gathers it has just issued.  Here the kernel orders DMA
-// and LDS reads itself (an explicit vmcnt wait and a barrier at the head of
-// each step; reads and DMA writes of one step touch disjoint buffers).  VMEM
-// operations the compiler does not see can only make its own (in-order)
-// vmcnt waits stricter, never looser.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_t)lds;
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
-}
-
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int V>
 using ic = std::integral_constant<int, V>;
@@ -182,7 +142,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
       int row;
       if (SPARSE) row = ring[(tile % (2 * IDS_CHUNK)) * KT + r];
       else row = kp < nkeys ? kp : -1;   // -1: past the end -> zero rows
-      rowoff[j] = (uint32_t)row * (uint32_t)ROWB;
+      rowoff[j] = (uint32_t)row * (uint32_t)ROWB + coff[j];
     }
   };
   // refill ring half (chunk & 1) with the ids of tiles [chunk*IDS_CHUNK, +IDS_CHUNK)
@@ -203,13 +163,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
     constexpr int BUF = decltype(buf_c)::value;
 #pragma unroll
     for (int j = 0; j < IPW; ++j)
-      dma16(rk, rowoff[j] + coff[j], lbase + BUF * STAGE_BYTES + (w * IPW + j) * 1024);
+      dma16(rk, rowoff[j], lbase + BUF * STAGE_BYTES + (w * IPW + j) * 1024);
   };
   auto issue_v = [&](auto buf_c, const uint32_t (&rowoff)[IPW]) {
     constexpr int BUF = decltype(buf_c)::value;
 #pragma unroll
     for (int j = 0; j < IPW; ++j)
-      dma16(rv, rowoff[j] + coff[j], lbase + BUF * STAGE_BYTES + TILE_BYTES + (w * IPW + j) * 1024);
+      dma16(rv, rowoff[j], lbase + BUF * STAGE_BYTES + TILE_BYTES + (w * IPW + j) * 1024);
   };
 
   // ---- per-lane LDS read offsets (buffer, key block and k-step are immediates) ----

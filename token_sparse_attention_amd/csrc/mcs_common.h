@@ -95,4 +95,45 @@ __device__ __forceinline__ int xcd_remap(int block, int total) {
   return xcd * base + (xcd < extra ? xcd : extra) + slot;
 }
 
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+// 16-byte chunk swizzle of a K or V row in LDS.  The gfx950 LDS has 64 banks of
+// 4 bytes, i.e. 16 bank groups of 16 bytes; a ds_read_b128 serves 16 lanes per
+// cycle and a ds_read_b64_tr_b16 32 lanes.  D = 128 (256-byte rows, bank
+// group = physical chunk): f maps any 16 consecutive rows to a permutation of
+// 0..15 (K fragment reads: 16 rows, one logical chunk) and the 4 rows of a
+// transpose read (rows 4a..4a+3) to 0, 4, 8, 12 (+ a constant), so their 4
+// consecutive chunks land in 16 distinct groups.  D = 64 (128-byte rows, two
+// rows per bank row): the same two properties with the row's half taken into
+// account.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Buffer resource of one head's K or V rows: loads at byte offsets at or past
+// `bytes` return zeros (rows past the end of a tile, ids outside [0, N)).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte buffer load per lane written straight to LDS: the wave writes
+// 1 KiB at lds (wave-uniform) + 16 * lane.
+//
+// Issued as inline assembly on purpose: the compiler cannot tell the LDS
+// range a DMA writes from the ranges the tile loop reads, and for the builtin
+// it places a full vmcnt wait before the next LDS read, which would make every
+// tile step wait for the loads it has just issued.  The kernels order DMA and
+// LDS reads themselves: an explicit vmcnt wait and a barrier before a buffer
+// is read, and the DMA and the reads of one step touch disjoint buffers.
+// VMEM operations the compiler does not see can only make its own (in-order)
+// vmcnt waits stricter, never looser.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_t)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace mcs
