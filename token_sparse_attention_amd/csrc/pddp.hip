@@ -176,124 +176,218 @@ __global__ __launch_bounds__(PD_NT) void pddp_moments(PddpParams p) {
   }
 }
 
-__device__ __forceinline__ float block_sum_256(float x, float* sh) {
-  // sum over a 256-thread workgroup, fixed order
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  __syncthreads();
-  if (lane == 0) sh[w] = x;
-  __syncthreads();
-  return sh[0] + sh[1] + sh[2] + sh[3];
-}
-
-template <int D>
+// Principal direction of one node per workgroup.  The node's second moments
+// live in registers in the MFMA accumulator layout of node_moments: wave w,
+// block b covers the 32x32 block (rb, cb) of sum(x x^T) with f = w*NBLK + b,
+// rb = f / (D/32), cb = f % (D/32), and lane (lq, hh) holds element e of it at
+// row rb*32 + 8*(e/4) + 4*hh + e%4, column cb*32 + lq.  The power iteration
+// runs on that layout: since the covariance is symmetric, y = C v is
+// y[c] = sum_r C[r][c] v[r], so every lane sums its 16 rows of one column,
+// the two half-waves are added with one lane swap, and the row blocks meet in
+// a small LDS array.  Two barriers per step; nothing D x D ever goes to LDS.
+// FROM_PARTS: the node's moments are summed from pddp_moments partials (large
+// nodes); otherwise the workgroup computes them itself.
+template <int D, bool FROM_PARTS>
 __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   constexpr int NBLK = (D / 32) * (D / 32) / 4;
+  constexpr int RB = D / 32;
   constexpr int CH = D / 8;
-  __shared__ float cov[D][D + 1];
-  __shared__ float mu[D], vec[D], nv[D];
-  __shared__ float sh[8];
-  __shared__ int ish[2];
   __shared__ MomentLds<D> L;
   __shared__ float sred[MSTEP / 4][D];
-
+  __shared__ float part[2][RB][D];
+  __shared__ float mu[D], vec[D];
+  __shared__ float red[4];
+  __shared__ int ish[2];
   const int slot = blockIdx.x, bh = blockIdx.y;
   int off, n, g;
   if (!node_geom(p.N, p.C, p.level, slot, off, n, g)) return;
   const size_t head = (size_t)bh * p.N;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
 
-  if (p.cpn > 1) {
-    // sum the node's chunk partials in chunk order
+  f32x16_t acc[NBLK];
+  if (FROM_PARTS) {
+    // sum the node's chunk partials in chunk order, straight into the layout
+    // (the chunk loop is outermost so every thread has 64 loads in flight)
     const int nch = (n + CHUNK_M - 1) / CHUNK_M;
     const float* __restrict__ base = p.part + ((size_t)bh * p.slots + (size_t)slot * p.cpn) * (D * D + D);
-    for (int i = tid; i < D * D + D; i += PD_NT) {
-      float s = 0.f;
-      for (int c = 0; c < nch; ++c) s += base[(size_t)c * (D * D + D) + i];
-      if (i < D * D) cov[i / D][i % D] = s;
-      else mu[i - D * D] = s;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) acc[b] = zero16();
+    float msum = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float* __restrict__ pc = base + (size_t)c * (D * D + D);
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc[b][e] += pc[(size_t)(rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + cb * 32 + lq];
+      }
+      if (tid < D) msum += pc[D * D + tid];
     }
+    if (tid < D) mu[tid] = msum;
   } else {
-    f32x16_t acc[NBLK];
     float sumx[8];
     node_moments<D>(p.q + head * D, p.perm + head + off, p.N, 0, n, L, acc, sumx);
-#pragma unroll
-    for (int b = 0; b < NBLK; ++b) {
-      const int f = w * NBLK + b;
-      const int rb = f / (D / 32), cb = f % (D / 32);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) cov[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)][cb * 32 + lq] = acc[b][e];
-    }
     if (tid < (MSTEP / 4) * CH) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) sred[tid / CH][(tid % CH) * 8 + e] = sumx[e];
     }
     __syncthreads();
     if (tid < D) {
-      float s = 0.f;
-      for (int qd = 0; qd < MSTEP / 4; ++qd) s += sred[qd][tid];
-      mu[tid] = s;
+      float sacc = 0.f;
+      for (int qd = 0; qd < MSTEP / 4; ++qd) sacc += sred[qd][tid];
+      mu[tid] = sacc;
     }
   }
   __syncthreads();
   const float inv_n = 1.f / (float)n;
   if (tid < D) mu[tid] *= inv_n;
   __syncthreads();
-  for (int i = tid; i < D * D; i += PD_NT) {
-    const int a = i / D, b = i % D;
-    cov[a][b] = cov[a][b] * inv_n - mu[a] * mu[b];
-  }
-  __syncthreads();
-
-  // start: the covariance column of largest diagonal (first on ties)
-  if (tid == 0) {
-    int best = 0;
-    float bv = cov[0][0];
-    for (int d = 1; d < D; ++d)
-      if (cov[d][d] > bv) {
-        bv = cov[d][d];
-        best = d;
-      }
-    ish[0] = best;
-  }
-  __syncthreads();
-  float x = tid < D ? cov[tid][ish[0]] : 0.f;
-  float nrm2 = block_sum_256(x * x, sh);
-  if (tid < D) vec[tid] = nrm2 > 0.f ? x * rsqrtf(nrm2) : (tid == 0 ? 1.f : 0.f);
-  __syncthreads();
-  const int iters = p.iters > 0 ? p.iters : DEFAULT_ITERS;
-  for (int it = 0; it < iters; ++it) {
-    float y = 0.f;
-    if (tid < D) {
-#pragma unroll 8
-      for (int e = 0; e < D; ++e) y = fmaf(cov[tid][e], vec[e], y);
+  // covariance = sum(x x^T)/n - mu mu^T, in place
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
+    const float mc = mu[cb * 32 + lq];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+      acc[b][e] = acc[b][e] * inv_n - mu[r] * mc;
     }
-    const float s2 = block_sum_256(y * y, sh);
-    if (s2 > 0.f && tid < D) nv[tid] = y * rsqrtf(s2);
-    else if (tid < D) nv[tid] = vec[tid];
-    __syncthreads();
-    if (tid < D) vec[tid] = nv[tid];
-    __syncthreads();
   }
-  // sign: largest-magnitude component positive (first on ties)
-  if (tid == 0) {
-    int best = 0;
-    float bv = fabsf(vec[0]);
-    for (int d = 1; d < D; ++d)
-      if (fabsf(vec[d]) > bv) {
-        bv = fabsf(vec[d]);
-        best = d;
-      }
-    ish[1] = vec[best] < 0.f ? 1 : 0;
+  // start: the covariance column of largest diagonal (first on ties); the
+  // diagonal goes through part[0]
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
+    if (rb == cb && hh == ((lq >> 2) & 1)) part[0][0][cb * 32 + lq] = acc[b][4 * (lq >> 3) + (lq & 3)];
   }
   __syncthreads();
-  const float sgn = ish[1] ? -1.f : 1.f;
-  const float vv = tid < D ? sgn * vec[tid] : 0.f;
-  const float muv = block_sum_256(tid < D ? mu[tid] * vv : 0.f, sh);
-  float* __restrict__ out = p.dir + ((size_t)bh * p.nodes + slot) * (D + 4);
-  if (tid < D) out[tid] = vv;
-  if (tid == 0) out[D] = muv;
+  if (w == 0) {
+    float bv = -INFINITY;
+    int bi = 0;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const float x = part[0][0][lane + 64 * k];
+      if (x > bv) {
+        bv = x;
+        bi = lane + 64 * k;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) ish[0] = bi;
+  }
+  __syncthreads();
+  {
+    const int best = ish[0];
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
+      if (cb * 32 + lq == best) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vec[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)] = acc[b][e];
+      }
+    }
+  }
+  __syncthreads();
+  // normalise the start column (wave 0; a zero column gives e_0)
+  if (w == 0) {
+    float y[D / 64], s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      y[k] = vec[lane + 64 * k];
+      s2 = fmaf(y[k], y[k], s2);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int c = lane + 64 * k;
+      vec[c] = s2 > 0.f ? y[k] * rsqrtf(s2) : (c == 0 ? 1.f : 0.f);
+    }
+  }
+  __syncthreads();
+  // Power iteration, one barrier per step: every wave forms y = C v from the
+  // row-block partials (buffer it & 1), takes |y| itself, and writes the new v
+  // only for the rows its own blocks read (vec rows are private to a wave from
+  // here on; a zero y leaves v unchanged).
+  const int iters = p.iters > 0 ? p.iters : DEFAULT_ITERS;
+  const int myrb = (w * NBLK) / RB;       // row block of this wave's blocks
+  for (int it = 0; it < iters; ++it) {
+    const int pb = it & 1;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
+      float y = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y = fmaf(acc[b][e], vec[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)], y);
+      y = halves_sum(y);
+      if (hh == 0) part[pb][rb][cb * 32 + lq] = y;
+    }
+    __syncthreads();
+    float y[D / 64], s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      float v = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) v += part[pb][rb][lane + 64 * k];
+      y[k] = v;
+      s2 = fmaf(v, v, s2);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+    if (s2 > 0.f) {
+      const float inv = rsqrtf(s2);
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        const int c = lane + 64 * k;
+        if ((c >> 5) == myrb) vec[c] = y[k] * inv;
+      }
+    }
+  }
+  // each row block of vec now holds v (written by the wave that owns it)
+  __syncthreads();
+  // sign: largest-magnitude component positive (first on ties); mu.v
+  if (w == 0) {
+    float bv = -1.f, mv = 0.f;
+    int bi = 0;
+    float sgnv = 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int c = lane + 64 * k;
+      const float x = vec[c];
+      if (fabsf(x) > bv) {
+        bv = fabsf(x);
+        bi = c;
+        sgnv = x;
+      }
+      mv = fmaf(mu[c], x, mv);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      const float os = __shfl_xor(sgnv, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+        sgnv = os;
+      }
+      mv += __shfl_xor(mv, o);
+    }
+    const float sgn = sgnv < 0.f ? -1.f : 1.f;
+    float* __restrict__ out = p.dir + ((size_t)bh * p.nodes + slot) * (D + 4);
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) out[lane + 64 * k] = sgn * vec[lane + 64 * k];
+    if (lane == 0) out[D] = sgn * mv;
+  }
 }
 
 template <int D>
@@ -339,8 +433,9 @@ __global__ __launch_bounds__(PD_NT) void pddp_project(PddpParams p) {
   }
 }
 
-__global__ __launch_bounds__(PD_NT) void pddp_split(PddpParams p) {
-  __shared__ RadixLds<PD_NT> L;
+template <int NT>
+__global__ __launch_bounds__(NT) void pddp_split(PddpParams p) {
+  __shared__ RadixLds<NT> L;
   const int slot = blockIdx.x, bh = blockIdx.y;
   int off, n, g;
   if (!node_geom(p.N, p.C, p.level, slot, off, n, g)) return;
@@ -352,8 +447,8 @@ __global__ __launch_bounds__(PD_NT) void pddp_split(PddpParams p) {
   auto key = [&](int i) -> uint32_t { return float_order_key(pr[i]); };
   uint32_t T;
   int need;
-  radix_select_smallest<PD_NT>(key, n, r, L, T, need);
-  ordered_compact<PD_NT>(key, n, T, need, L, [&](int i, bool sel, int rank) {
+  radix_select_smallest<NT>(key, n, r, L, T, need);
+  ordered_compact<NT>(key, n, T, need, L, [&](int i, bool sel, int rank) {
     const int pos = sel ? rank : r + rank;   // < n by construction; kept as a bound
     if (pos < n) out[pos] = ids[i];
   });
@@ -410,9 +505,12 @@ static hipError_t group_levels(PddpParams p, int BH, const GroupPlan& pl, hipStr
     if (p.cpn > 1) {
       hipLaunchKernelGGL(pddp_moments<D>, dim3(p.cpn, nodes, BH), dim3(PD_NT), 0, s, p);
     }
-    hipLaunchKernelGGL(pddp_direction<D>, dim3(nodes, BH), dim3(PD_NT), 0, s, p);
+    if (p.cpn > 1) hipLaunchKernelGGL((pddp_direction<D, true>), dim3(nodes, BH), dim3(PD_NT), 0, s, p);
+    else hipLaunchKernelGGL((pddp_direction<D, false>), dim3(nodes, BH), dim3(PD_NT), 0, s, p);
     hipLaunchKernelGGL(pddp_project<D>, dim3(p.cpn, nodes, BH), dim3(PD_NT), 0, s, p);
-    hipLaunchKernelGGL(pddp_split, dim3(nodes, BH), dim3(PD_NT), 0, s, p);
+    // large nodes take a 1024-thread selection, small ones 256
+    if (maxn > 8192) hipLaunchKernelGGL(pddp_split<1024>, dim3(nodes, BH), dim3(1024), 0, s, p);
+    else hipLaunchKernelGGL(pddp_split<PD_NT>, dim3(nodes, BH), dim3(PD_NT), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
