@@ -229,13 +229,196 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__
   });
 }
 
+// Adds one to hist[bin] for every active lane.  Lanes that share a bin with
+// the lowest pending lane are counted with one atomic for the lot (done twice,
+// which takes the bins most lanes fall in: mass values mostly share their
+// leading key bits); the rest add their own.
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t bin, int lane) {
+  uint64_t pend = __ballot(active);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (pend == 0) break;
+    const int leader = __ffsll((unsigned long long)pend) - 1;
+    const uint32_t lb = __shfl(bin, leader);
+    const uint64_t same = __ballot(active && bin == lb) & pend;
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    pend &= ~same;
+  }
+  if ((pend >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+}
+
+// The same selection with the whole row held on chip (element i of the row in
+// slot i / TOPK_NT of thread i % TOPK_NT; the first RSLOTS slots in
+// registers, the rest in LDS): the row is read from memory once instead of
+// once per radix pass and once more for the compaction.  Rows of up to
+// TOPK_NT * SLOTS values.  Slots past the row end hold the largest key (that
+// of a zero score): they rank after every element of the row, so they never
+// change the K-th key (K <= n); the compaction skips them.  The compaction
+// counts, per round of TOPK_NT positions and per wave, the keys below and
+// equal to the threshold, scans those counts once in position order, and then
+// places every chosen id without further synchronisation.
+template <int SLOTS, int RSLOTS>
+__global__ __launch_bounds__(TOPK_NT) void topk_reg_kernel(const float* __restrict__ scores,
+                                                          int32_t* __restrict__ idx, int n, int K) {
+  constexpr int NWV = TOPK_NT / 64;
+  constexpr int HBINS = 4096;
+  __shared__ uint32_t hist[HBINS];
+  __shared__ uint32_t wtot[NWV];
+  __shared__ uint32_t sel_digit, sel_below;
+  __shared__ uint32_t kl[SLOTS - RSLOTS][TOPK_NT];
+  __shared__ uint32_t cnt[2][SLOTS * NWV];   // [lt | eq][round * NWV + wave], scanned in place
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const size_t row = blockIdx.x;
+  const uint32_t* __restrict__ x = reinterpret_cast<const uint32_t*>(scores) + row * (size_t)n;
+  int32_t* __restrict__ out = idx + row * (size_t)K;
+  const int nslots = (n + TOPK_NT - 1) / TOPK_NT;
+  // larger score -> smaller key; -0.0 (and any negative, which is not allowed) -> as 0
+  auto to_key = [](uint32_t u) -> uint32_t { return ~((u & 0x80000000u) ? 0u : u); };
+  // the LDS slots arrive by DMA (raw score bits; reads past the row end give
+  // 0, a zero score), all in flight together with the register slots' loads
+  const __amdgpu_buffer_rsrc_t rrow = head_rsrc(x, (uint32_t)n * 4u);
+  for (int k = RSLOTS; k < nslots; ++k)
+    dma4(rrow, (uint32_t)(k * TOPK_NT + tid) * 4u, &kl[k - RSLOTS][w * 64]);
+  uint32_t kv[RSLOTS];
+#pragma unroll
+  for (int k = 0; k < RSLOTS; ++k) {
+    const int i = k * TOPK_NT + tid;
+    kv[k] = to_key(i < n ? x[i] : 0u);
+  }
+  wait_vmem_all();
+  __syncthreads();
+  auto lkey = [&](int k) -> uint32_t { return to_key(kl[k - RSLOTS][tid]); };
+  // radix select of the K-th smallest key in three passes of 12, 12 and 8
+  // bits over one shared histogram: after the first pass few keys still
+  // match the prefix, so the later passes cost little more than a compare
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = K;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const uint32_t dmask = pass == 2 ? 255u : 4095u;
+    for (int i = tid; i < HBINS; i += TOPK_NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < RSLOTS; ++k)
+      if (k < nslots) hist_add(hist, (kv[k] & pmask) == prefix, (kv[k] >> shift) & dmask, lane);
+#pragma unroll 2
+    for (int k = RSLOTS; k < nslots; ++k) {
+      const uint32_t key = lkey(k);
+      hist_add(hist, (key & pmask) == prefix, (key >> shift) & dmask, lane);
+    }
+    __syncthreads();
+    // the bin holding the remaining-th key: thread t owns bins 4t .. 4t+3
+    uint32_t c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = hist[4 * tid + q];
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wtot[w] = incl;
+    __syncthreads();
+    uint32_t wbase = 0;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww)
+      if (ww < w) wbase += wtot[ww];
+    const uint32_t excl = wbase + incl - local;
+    if (excl < (uint32_t)remaining && (uint32_t)remaining <= excl + local) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (acc + c[q] >= (uint32_t)remaining) {
+          sel_digit = 4 * tid + q;
+          sel_below = acc;
+          break;
+        }
+        acc += c[q];
+      }
+    }
+    __syncthreads();
+    prefix |= sel_digit << shift;
+    pmask |= dmask << shift;
+    remaining -= (int)sel_below;
+  }
+  const uint32_t T = prefix;
+  const int need = remaining;
+
+  // compaction, step 1: per round and wave, the keys below and equal to T
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto count = [&](int k, uint32_t key) {
+    const bool valid = k * TOPK_NT + tid < n;
+    const uint64_t blt = __ballot(valid && key < T), beq = __ballot(valid && key == T);
+    if (lane == 0) {
+      cnt[0][k * NWV + w] = (uint32_t)__popcll(blt);
+      cnt[1][k * NWV + w] = (uint32_t)__popcll(beq);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < RSLOTS; ++k)
+    if (k < nslots) count(k, kv[k]);
+  for (int k = RSLOTS; k < nslots; ++k) count(k, lkey(k));
+  __syncthreads();
+  // step 2: exclusive scans of both count arrays in position order (wave 0
+  // scans the lt counts, wave 1 the eq counts; each lane owns a contiguous run)
+  if (w < 2) {
+    uint32_t* c = cnt[w];
+    const int total = nslots * NWV;
+    const int per = (total + 63) / 64;
+    const int b0 = lane * per, b1 = min(total, b0 + per);
+    uint32_t local = 0;
+    for (int j = b0; j < b1; ++j) local += c[j];
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    uint32_t run = incl - local;
+    for (int j = b0; j < b1; ++j) {
+      const uint32_t v = c[j];
+      c[j] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  // step 3: place every chosen id: rank = #(keys < T before it) +
+  // min(#(keys == T before it), need)
+  auto place = [&](int k, uint32_t key) {
+    const int i = k * TOPK_NT + tid;
+    const bool valid = i < n;
+    const bool lt = valid && key < T;
+    const bool eq = valid && key == T;
+    const uint64_t blt = __ballot(lt), beq = __ballot(eq);
+    const uint32_t lt_before = cnt[0][k * NWV + w] + (uint32_t)__popcll(blt & lt_mask);
+    const uint32_t eq_before = cnt[1][k * NWV + w] + (uint32_t)__popcll(beq & lt_mask);
+    if (lt || (eq && eq_before < (uint32_t)need)) {
+      const uint32_t rank = lt_before + (eq_before < (uint32_t)need ? eq_before : (uint32_t)need);
+      if (rank < (uint32_t)K) out[rank] = i;   // rank < K by construction; kept as a bound
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < RSLOTS; ++k)
+    if (k < nslots) place(k, kv[k]);
+  for (int k = RSLOTS; k < nslots; ++k) place(k, lkey(k));
+}
+
+constexpr int TOPK_REG_SLOTS = 80;    // rows of up to 81920 values
+constexpr int TOPK_REG_RSLOTS = 50;   // ... the first 50 slots in registers, the rest in LDS
+
 hipError_t run_topk(const float* scores, int32_t* idx, int64_t rows, int n, int K,
                     hipStream_t s) {
   const int64_t max_grid = 1 << 30;
+  const bool in_regs = n <= TOPK_NT * TOPK_REG_SLOTS;
   for (int64_t r0 = 0; r0 < rows; r0 += max_grid) {
     const int64_t nr = rows - r0 < max_grid ? rows - r0 : max_grid;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)nr), dim3(TOPK_NT), 0, s,
-                       scores + r0 * (int64_t)n, idx + r0 * (int64_t)K, n, K);
+    if (in_regs)
+      hipLaunchKernelGGL((topk_reg_kernel<TOPK_REG_SLOTS, TOPK_REG_RSLOTS>), dim3((unsigned)nr), dim3(TOPK_NT), 0, s,
+                         scores + r0 * (int64_t)n, idx + r0 * (int64_t)K, n, K);
+    else
+      hipLaunchKernelGGL(topk_kernel, dim3((unsigned)nr), dim3(TOPK_NT), 0, s,
+                         scores + r0 * (int64_t)n, idx + r0 * (int64_t)K, n, K);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
