@@ -115,6 +115,23 @@ def measured_traffic(workload: str, kernel_prefix: str):
     return None
 
 
+def measured_util(workload: str, kernel_prefix: str):
+    """Shader clock and MFMA-busy share of a kernel from the committed counter
+    summary, if it still describes the current kernel sources (else None)."""
+    from token_sparse_attention_amd import pmc
+    path = os.path.join(ROOT, "profiles", f"pmc_util_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != pmc.source_hash():
+        return None
+    for name, v in d["kernels"].items():
+        if name.startswith(kernel_prefix):
+            return v
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -250,6 +267,15 @@ def main():
         "dense_tflops": round(dense_flops / (ms["dense_lse"] * 1e-3) / 1e12, 2),
         "select_tflops": round(accounting.select_flops(B, H, N, D) / (ms["select"] * 1e-3) / 1e12, 2),
     }
+    util = measured_util(args.workload, f"attn_kernel<{D}, {w.C // 32}, true, true")
+    if util is not None:
+        # the clock this kernel ran at under the counters (GRBM_GUI_ACTIVE over
+        # the dispatch time) and the bf16 MFMA peak at that clock
+        peak_clk = PEAK_BF16_TFLOPS * util["clock_ghz"] / 2.4
+        out["roofline"].update({"measured_clock_ghz": round(util["clock_ghz"], 3),
+                                "peak_at_measured_clock": round(peak_clk, 1),
+                                "frac_at_measured_clock": round(achieved / peak_clk, 4),
+                                "mfma_busy_counter": round(util["mfma_busy"], 4)})
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(args, w, x0, K, scale)

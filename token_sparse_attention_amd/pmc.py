@@ -1,6 +1,7 @@
 """HBM traffic of the hot-path kernels from rocprofv3 counter runs.
 
     python -m token_sparse_attention_amd.pmc FETCH_DIR WRITE_DIR OUT.json [--workload large]
+    python -m token_sparse_attention_amd.pmc --util UTIL_DIR OUT.json
 
 FETCH_DIR and WRITE_DIR are the output directories of two runs of
 
@@ -13,6 +14,16 @@ kernel of known size measured in the same runs: residual_kernel, which reads
 two bf16 tensors of B*H*N*D elements and writes one.  The result, per kernel,
 is written to OUT.json together with a hash of the kernel sources, so that
 bench.py reports the traffic only while the kernels are unchanged.
+
+--util summarises one run of
+
+    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES \
+        GRBM_GUI_ACTIVE -d UTIL_DIR -o pmc --output-format csv -- python3 bench.py ...
+
+per kernel: the average shader clock over the dispatch (GRBM_GUI_ACTIVE, summed
+over the 8 XCDs, divided by the dispatch time), the share of SIMD cycles in
+which the MFMA unit was busy, and the share in which a plain VALU
+instruction issued while it was (co-execution).
 """
 from __future__ import annotations
 
@@ -68,7 +79,51 @@ def summarize(fetch_dir: str, write_dir: str, workload: str) -> dict:
             "write_scale": f_write, "source_hash": source_hash(), "kernels": kernels}
 
 
+N_XCD = 8
+N_SIMD = 256 * 4
+
+
+def utilisation(util_dir: str) -> dict:
+    rows = defaultdict(lambda: defaultdict(float))
+    times = defaultdict(dict)
+    for f in glob.glob(os.path.join(util_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("mcs::", "")
+                d = r["Dispatch_Id"]
+                rows[(name, d)][r["Counter_Name"]] += float(r["Counter_Value"])
+                times[(name, d)] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    acc = defaultdict(lambda: defaultdict(float))
+    for (name, d), c in rows.items():
+        t0, t1 = times[(name, d)]
+        dt = (t1 - t0) * 1e-9
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        if dt <= 0 or cyc <= 0:
+            continue
+        a = acc[name]
+        a["n"] += 1
+        a["ms"] += dt * 1e3
+        a["clock_ghz"] += cyc / dt / 1e9
+        a["mfma_busy"] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (N_SIMD * cyc)
+        a["coexec"] += c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / (N_SIMD * cyc)
+        a["cu_busy"] += c.get("SQ_BUSY_CU_CYCLES", 0.0) * 4 / (256 * cyc)
+    out = {}
+    for name, a in acc.items():
+        n = a.pop("n")
+        out[name] = {k: v / n for k, v in a.items()}
+        out[name]["dispatches"] = int(n)
+    return {"source_hash": source_hash(), "kernels": out}
+
+
 def main(argv):
+    if argv and argv[0] == "--util":
+        out = utilisation(argv[1])
+        with open(argv[2], "w") as f:
+            json.dump(out, f, indent=1)
+        for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["ms"]):
+            print(f"{k:48s} {v['ms']:9.3f} ms  clock {v['clock_ghz']:.3f} GHz  MFMA busy {100 * v['mfma_busy']:5.1f}%"
+                  f"  co-exec {100 * v['coexec']:5.1f}%")
+        return 0
     if len(argv) < 3:
         print(__doc__)
         return 2
