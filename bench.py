@@ -11,9 +11,12 @@ torch.cuda.synchronize(); every stage is also timed with HIP events on the
 stream the library launches on (torch's current stream).
 
 The headline metric is the token-sparse attention speedup over this library's
-own dense attention at the same shape (reuse-step sparse kernel vs the anchor's
-dense kernel), with the sparse kernel's MFMA-roofline fraction at the
-density-scaled FLOP count 4*B*H*N*K*D.  One JSON line is printed.
+own dense attention at the same shape (reuse-step sparse kernel vs the dense
+kernel without LSE; the anchor's dense pass with LSE is reported beside it),
+with the sparse kernel's MFMA-roofline fraction at the density-scaled FLOP
+count 4*B*H*N*K*D.  One JSON line is printed.  --all-workloads measures every
+workload and density instead (one line each), with the anchor-path cost and
+the 50-step schedule with an anchor every 10 steps.
 """
 from __future__ import annotations
 
@@ -47,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=32768)
     ap.add_argument("--cpu-sample-groups", type=int, default=591)
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="every workload and density (one JSON line each) instead of the headline one")
     return ap.parse_args()
 
 
@@ -132,28 +137,24 @@ def measured_util(workload: str, kernel_prefix: str):
     return None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
-              "head with no exchange, see the design notes", file=sys.stderr)
-        sys.exit(2)
+def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
+    """One workload at one density: W warm-up and K timed steps; returns the
+    result object (without the CPU baseline)."""
     import torch
 
     from token_sparse_attention_amd import accounting, binding, synth
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = synth.WORKLOADS[args.workload]
-    s = args.density if args.density is not None else w.densities[0]
+    w = synth.WORKLOADS[workload]
+    s = density if density is not None else w.densities[0]
     K = accounting.k_from_density(s, w.N)
     G = accounting.num_groups(w.N, w.C)
     scale = 1.0 / math.sqrt(w.D)
 
     t0 = time.time()
-    x0 = synth.generate(args.workload)
-    x1 = synth.drift(args.workload, x0, step=1)
-    log(args, f"[bench] inputs {args.workload} generated in {time.time() - t0:.1f}s")
+    x0 = synth.generate(workload)
+    x1 = synth.drift(workload, x0, step=1)
+    log(args, f"[bench] inputs {workload} generated in {time.time() - t0:.1f}s")
 
     def dev_bf16(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -193,19 +194,19 @@ def main():
         binding.sparse_attn(q1, k1, v1, perm, kv_idx, w.C, residual=res, scale=scale, out=o_reuse)
         mark(6)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     log(args, "[bench] warm-up done")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(args, f"[bench] {args.steps} timed steps in {wall:.3f}s")
+    log(args, f"[bench] {steps} timed steps in {wall:.3f}s")
 
     per_stage = {name: [] for name in stages}
     for ev in events:
@@ -214,7 +215,7 @@ def main():
     ms = {name: float(np.mean(v)) for name, v in per_stage.items()}
 
     # the dense baseline without LSE, same shape (isolated launches)
-    reps = max(3, args.steps)
+    reps = max(3, steps)
     e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     o_tmp = torch.empty_like(q0)
     binding.dense_attn(q0, k0, v0, scale, out=o_tmp)
@@ -224,34 +225,34 @@ def main():
     e0[reps].record()
     torch.cuda.synchronize()
     dense_nolse_ms = float(np.mean([e0[i].elapsed_time(e0[i + 1]) for i in range(reps)]))
+    speedup = dense_nolse_ms / ms["sparse_reuse"]
 
     sparse_flops = accounting.sparse_flops(B, H, N, K, D)
     dense_flops = accounting.dense_flops(B, H, N, D)
     t_sparse = ms["sparse_reuse"] * 1e-3
     achieved = sparse_flops / t_sparse / 1e12
-    speedup = ms["dense_lse"] / ms["sparse_reuse"]
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = wall / steps * 1e3
 
     out = {
         "metric": METRIC,
         "value": round(speedup, 4),
-        "unit": "x (own dense attention ms / token-sparse attention ms, same shape)",
+        "unit": "x (own dense attention ms, no LSE / token-sparse attention ms, same shape)",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: B={B} H={H} N={N} D={D} C={w.C} density={s} K={K} G={G}",
+        "config": {"workload": f"{workload}: B={B} H={H} N={N} D={D} C={w.C} density={s} K={K} G={G}",
                    "B": B, "H": H, "N": N, "D": D, "C": w.C, "density": s, "K": K,
                    "step": "anchor (group, dense+lse, select, sparse, residual) + reuse (sparse + residual)",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload, f"attn_kernel<{D}, {w.C // 32}, true, true"),
+                     "traffic": measured_traffic(workload, f"attn_kernel<{D}, {w.C // 32}, true, true"),
                      "kernel": "attn_kernel (sparse, residual epilogue)",
                      "per_launch_flops": sparse_flops, "avg_launch_ms": round(ms["sparse_reuse"], 4),
                      "algorithmic_bytes": accounting.sparse_compulsory_bytes(B, H, N, K, D, w.C),
@@ -261,13 +262,13 @@ def main():
                            "frac": round(dense_flops / (ms["dense_lse"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "stage_ms": {k: round(v, 4) for k, v in ms.items()},
         "dense_nolse_ms": round(dense_nolse_ms, 4),
-        "speedup_vs_dense_nolse": round(dense_nolse_ms / ms["sparse_reuse"], 4),
+        "speedup_vs_dense_with_lse": round(ms["dense_lse"] / ms["sparse_reuse"], 4),
         "ideal_speedup": round(N / K, 4),
         "efficiency_vs_ideal": round(speedup * K / N, 4),
         "dense_tflops": round(dense_flops / (ms["dense_lse"] * 1e-3) / 1e12, 2),
         "select_tflops": round(accounting.select_flops(B, H, N, D) / (ms["select"] * 1e-3) / 1e12, 2),
     }
-    util = measured_util(args.workload, f"attn_kernel<{D}, {w.C // 32}, true, true")
+    util = measured_util(workload, f"attn_kernel<{D}, {w.C // 32}, true, true")
     if util is not None:
         # the clock this kernel ran at under the counters (GRBM_GUI_ACTIVE over
         # the dispatch time) and the bf16 MFMA peak at that clock
@@ -276,10 +277,44 @@ def main():
                                 "peak_at_measured_clock": round(peak_clk, 1),
                                 "frac_at_measured_clock": round(achieved / peak_clk, 4),
                                 "mfma_busy_counter": round(util["mfma_busy"], 4)})
+    # anchor-path cost, and the schedule of the long-video setting: 50 steps
+    # with an anchor every 10 (5 anchors, 45 reuse steps)
+    t_anchor = sum(ms[k] for k in ("group", "dense_lse", "select", "sparse_anchor", "residual"))
+    out["anchor_ms"] = round(t_anchor, 4)
+    sched = (5 * t_anchor + 45 * ms["sparse_reuse"]) / 50
+    out["schedule_50x10"] = {"mean_step_ms": round(sched, 4),
+                             "speedup_vs_50_dense": round(dense_nolse_ms / sched, 4),
+                             "anchor_overhead_vs_dense": round(5 * (t_anchor - dense_nolse_ms) / (50 * dense_nolse_ms), 4)}
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(args, w, x0, K, scale)
         log(args, f"[bench] cpu baseline in {time.time() - t0:.1f}s")
+    del x0, x1
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+ALL_CONFIGS = [("tiny", 0.25), ("small", 0.20), ("large", 0.20), ("long", 0.25), ("long", 0.15), ("asset3d", 0.15)]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "head with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.all_workloads:
+        # one JSON line per (workload, density); no CPU baseline
+        args.no_cpu_baseline = True
+        for wl, dens in ALL_CONFIGS:
+            out = measure(args, wl, dens, args.steps, args.warmup)
+            print(json.dumps(out), flush=True)
+        return
+    out = measure(args, args.workload, args.density, args.steps, args.warmup)
     print(json.dumps(out), flush=True)
 
 
