@@ -90,8 +90,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][KT * D];
   char* const lbase = reinterpret_cast<char*>(&lds[0][0][0]);
   // sparse: ring of kv ids, two halves of IDS_CHUNK tiles, refilled by DMA
-  // a whole chunk ahead so id latency never reaches the tile loop
-  constexpr int IDS_CHUNK = 32;                       // tiles per ring half
+  // a whole chunk ahead so id latency never reaches the tile loop (D = 64:
+  // a half-size ring keeps the workgroup at 40 KB, four per CU)
+  constexpr int IDS_CHUNK = D == 64 ? 16 : 32;        // tiles per ring half
   constexpr int RING_IDS = SPARSE ? 2 * IDS_CHUNK * KT : 4;
   __shared__ __attribute__((aligned(1024))) int32_t ring[RING_IDS];
 
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   __amdgpu_buffer_rsrc_t rids;
   if (SPARSE) rids = head_rsrc(ids, (uint32_t)p.K * 4u);
   auto refill_ids = [&](int chunk) {
-    constexpr int BYTES = IDS_CHUNK * KT * 4;           // 8 KiB per half
+    constexpr int BYTES = IDS_CHUNK * KT * 4;           // bytes per half
     constexpr int PER_WAVE = BYTES / 1024 / NW;
     char* half = reinterpret_cast<char*>(&ring[0]) + (chunk & 1) * BYTES;
 #pragma unroll
