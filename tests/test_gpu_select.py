@@ -35,6 +35,29 @@ def test_topk_bit_exact(mcs, rows, n, K, ties):
         np.testing.assert_array_equal(got[r], oracle.topk_indices(scores[r], K))
 
 
+@pytest.mark.parametrize("rows,n,K", [(2, 81920, 40000), (2, 81921, 81921), (2, 51201, 1), (2, 51200, 51200),
+                                      (2, 118800, 29696)])
+def test_topk_row_sizes(mcs, rows, n, K):
+    """Rows at the edges of the on-chip kernel (all slots in registers, the
+    first LDS slot partly filled, the largest on-chip row) and past it (the
+    streaming kernel), with ties and zeros."""
+    scores = synth.mass_rows(rows, n, seed=7 * n + K, ties=True)
+    got = mcs.topk(to_dev(scores), K).cpu().numpy()
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r], oracle.topk_indices(scores[r], K))
+
+
+@pytest.mark.parametrize("n", [300, 60000, 81920])
+def test_topk_zero_rows_take_first_ids(mcs, n):
+    """All-zero rows: the K chosen ids are the first K (equal values go to the
+    smaller id), whatever the slots past the row end hold."""
+    scores = np.zeros((2, n), dtype=np.float32)
+    K = n // 2 + 1
+    got = mcs.topk(to_dev(scores), K).cpu().numpy()
+    for r in range(2):
+        np.testing.assert_array_equal(got[r], np.arange(K))
+
+
 def test_topk_all_equal_and_zero(mcs):
     scores = np.zeros((2, 300), dtype=np.float32)
     scores[1] = 0.25
