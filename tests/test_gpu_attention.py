@@ -54,6 +54,38 @@ def test_dense_large_logits(mcs):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=2e-3)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_dense_reference_moves_many_times(mcs, D):
+    """Scores climb by ~4.5 (6.5 in log2 units) per 64-key tile, so the
+    running reference maximum moves again and again (O and the sums are
+    rescaled each time) and the last tile dominates the softmax."""
+    q, k, v = synth.growing_scores(1000, D, seed=31, step=1.5)
+    o, lse = mcs.dense_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), 1.0, want_lse=True)
+    o32 = mcs.dense_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), 1.0, out_dtype=torch.float32)
+    ref_o, ref_lse = oracle.dense_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), 1.0)
+    assert ref_lse.max() > 60.0          # the regime the test is about
+    assert_output_close(o32.cpu().numpy().astype(np.float64), ref_o, "dense O (fp32 out)")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=2e-3)
+
+
+@pytest.mark.parametrize("ascending", [True, False])
+def test_sparse_reference_moves_many_times(mcs, ascending):
+    """The same climbing scores through gathered ids: ascending ids make each
+    later tile outrank the earlier ones (the reference moves), descending ids
+    put the largest scores in the first tile (it never moves)."""
+    N, D, C, K = 1000, 128, 128, 400
+    q, k, v = synth.growing_scores(N, D, seed=32, step=1.5)
+    G = accounting.num_groups(N, C)
+    perm = synth.random_perm(1, 1, N, seed=33)
+    idx = synth.random_index_sets(1, 1, G, K, N, seed=34)
+    if not ascending:
+        idx = np.ascontiguousarray(idx[..., ::-1])
+    o = mcs.sparse_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), to_dev(perm), to_dev(idx), C, scale=1.0,
+                        out_dtype=torch.float32)
+    ref = oracle.sparse_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), perm, idx, C, 1.0)
+    assert_output_close(o.cpu().numpy().astype(np.float64), ref, "sparse O (fp32 out)")
+
+
 SPARSE_CASES = [
     # B, H, N, D, C, K
     (1, 2, 1000, 128, 128, 200),

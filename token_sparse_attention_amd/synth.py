@@ -268,6 +268,23 @@ def stratified_index_sets(B: int, H: int, G: int, K: int, N: int, seed: int) -> 
     return out.reshape(B, H, G, K)
 
 
+def growing_scores(N: int, D: int, seed: int, step: float, tile: int = 64):
+    """bf16 bits of q, k, v [1, 1, N, D] whose scores q.k grow tile by tile.
+
+    Every query is 3u + 0.3 N(0,1) and key j is (step * (j // tile)) u +
+    0.3 N(0,1) for the unit vector u = (1, ..., 1)/sqrt(D), so with a unit
+    scale the scores of key tile t sit near 3 * step * t: a later tile
+    outranks all earlier ones by a wide margin.  v ~ N(0,1).
+    """
+    r = _rng(9400, seed)
+    u = np.full(D, 1.0 / np.sqrt(D))
+    q = 3.0 * u + 0.3 * r.standard_normal((1, 1, N, D))
+    t = (np.arange(N) // tile).astype(np.float64)
+    k = (step * t)[:, None] * u + 0.3 * r.standard_normal((1, 1, N, D))
+    v = r.standard_normal((1, 1, N, D))
+    return tuple(to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+
+
 def mass_rows(rows: int, N: int, seed: int, ties: bool = True) -> np.ndarray:
     """Non-negative float32 score rows for top-K tests, optionally with many ties."""
     r = _rng(9300, seed)
