@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=32768)
     ap.add_argument("--cpu-sample-groups", type=int, default=591)
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--offload-layers", type=int, default=0,
+                    help="time reuse steps over this many layers with the anchor cache resident vs offloaded")
     ap.add_argument("--all-workloads", action="store_true",
                     help="every workload and density (one JSON line each) instead of the headline one")
     return ap.parse_args()
@@ -295,6 +297,73 @@ def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
     return out
 
 
+def measure_offload(args, workload: str, layers: int, steps: int) -> dict:
+    """Reuse steps over `layers` attention layers whose anchor entries (perm,
+    kv ids, residual) are resident in HBM or offloaded to pinned host memory
+    with the next layer prefetched during the current layer's attention."""
+    import torch
+
+    from token_sparse_attention_amd import accounting, binding, synth
+    from token_sparse_attention_amd.cache import AnchorCache
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[workload]
+    s = w.densities[0]
+    K = accounting.k_from_density(s, w.N)
+    scale = 1.0 / math.sqrt(w.D)
+    x0 = synth.generate(workload)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = (dev_bf16(x0[t]) for t in "qkv")
+    st = binding.anchor_step(q, k, v, w.C, K, scale)
+    out_buf = torch.empty_like(q)
+    res = {}
+    for offload in (False, True):
+        cache = AnchorCache(layers, offload=offload)
+        for l in range(layers):          # every layer holds a copy of the same entry
+            cache.put(l, st["perm"], st["kv_idx"], st["residual"])
+        torch.cuda.synchronize()
+
+        def reuse_step():
+            for l in range(layers):
+                e = cache.get(l)
+                binding.sparse_attn(q, k, v, e.perm, e.kv_idx, w.C, residual=e.residual, scale=scale, out=out_buf)
+
+        reuse_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            reuse_step()
+        torch.cuda.synchronize()
+        res[offload] = (time.perf_counter() - t0) / (steps * layers) * 1e3
+        del cache
+    # the copy of one entry alone (host -> device, pinned)
+    host = [t.cpu().pin_memory() for t in (st["perm"], st["kv_idx"], st["residual"])]
+    dst = [torch.empty_like(t) for t in (st["perm"], st["kv_idx"], st["residual"])]
+    nbytes = sum(t.numel() * t.element_size() for t in host)
+    for d_, h_ in zip(dst, host):
+        d_.copy_(h_, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        for d_, h_ in zip(dst, host):
+            d_.copy_(h_, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    t_copy = e0.elapsed_time(e1) / steps
+    t_res, t_off = res[False], res[True]
+    hidden = (t_res + t_copy - t_off) / t_copy
+    return {"mode": "anchor-cache offload", "workload": workload, "layers": layers, "density": s, "K": K,
+            "entry_bytes": nbytes, "h2d_ms_per_entry": round(t_copy, 3),
+            "h2d_gbps": round(nbytes / (t_copy * 1e-3) / 1e9, 1),
+            "reuse_ms_per_layer_resident": round(t_res, 3), "reuse_ms_per_layer_offloaded": round(t_off, 3),
+            "transfer_hidden_fraction": round(max(0.0, min(1.0, hidden)), 3),
+            "flop_per_byte": round(accounting.sparse_flops(w.B, w.H, w.N, K, w.D) / nbytes, 1)}
+
+
 ALL_CONFIGS = [("tiny", 0.25), ("small", 0.20), ("large", 0.20), ("long", 0.25), ("long", 0.15), ("asset3d", 0.15)]
 
 
@@ -307,6 +376,9 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.offload_layers > 0:
+        print(json.dumps(measure_offload(args, args.workload, args.offload_layers, max(2, args.steps))), flush=True)
+        return
     if args.all_workloads:
         # one JSON line per (workload, density); no CPU baseline
         args.no_cpu_baseline = True
