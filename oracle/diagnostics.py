@@ -1,4 +1,4 @@
-"""Diagnostic selectors of the pages, in plain fp64 numpy (test infrastructure).
+"""Diagnostic selectors and groupings of the pages, in plain fp64 numpy.
 
 TEST INFRASTRUCTURE ONLY, like the rest of ``oracle``: only tests/ and the
 script ``oracle/diagnose.py`` use it; it imports nothing from the HIP path.
@@ -22,20 +22,40 @@ keeps, averaged over queries) and by the relative L1 error of the output when
 attention is renormalised over the selected keys (ai.info "Main Findings":
 token granularity improves both at matched density).
 
+The same pages set PDDP against k-means grouping: k-means gives clusters of
+unequal size, and padding every cluster to whole tiles makes the interactions
+actually computed exceed the nominal budget (ai.info "Main Findings", the
+alignment inflation factor of k-means for blocks and for tokens; wispaper.ai
+"Token-level selection needs tile-aligned query groups"; the agihunt.info
+method paragraphs).  ``kmeans`` and ``alignment_inflation`` measure that.
+
 Readings of what the pages leave open (listed in the design notes as well):
   D1 KV blocks are 64 consecutive keys (the kernels' key tile); the last one
      may be short;
-  D2 a query block is a query group of C queries: C consecutive queries
-     ("contiguous"), or a PDDP group;
+  D2 a query block is one query group: C consecutive queries ("contiguous"),
+     a PDDP group, or a k-means cluster of any size;
   D3 the budget is K = 128*floor(s*N/128) keys per query block (or per query),
      i.e. K/64 KV blocks for the block selectors;
   D4 recall = mean_i sum_{j in S(i)} P_ij; output error = sum |O_S - O| /
      sum |O| over all queries and channels, O_S renormalised over S(i), no
      residual;
   D5 mean-pooled score of KV block b for query block g: scale * mean(q_g) .
-     mean(k_b); ties in every ranking go to the smaller id.
+     mean(k_b); ties in every ranking go to the smaller id;
+  D6 k-means is Lloyd's algorithm (squared Euclidean distance, assignment to
+     the nearest centre with ties to the smaller centre id, centre = mean of
+     its members, an empty cluster keeps its centre) for a fixed number of
+     rounds from given initial centres; queries form ceil(N/C) clusters
+     (as many as PDDP groups), keys ceil(N/64) clusters;
+  D7 alignment inflation = the rows actually computed when every cluster is
+     padded to whole tiles, over the real rows: sum_c ceil(n_c/T)*T / N.  Token
+     selection pads only the query clusters (T = C); block selection over
+     k-means key clusters also pads the key clusters (T = 64), so its factor is
+     the product of the query and key factors (every key cluster equally
+     likely to be chosen).
 """
 from __future__ import annotations
+
+from collections.abc import Sequence
 
 import numpy as np
 
@@ -64,47 +84,102 @@ def block_sums(x: np.ndarray, N: int) -> np.ndarray:
     return pad.reshape(nb, KV_BLOCK).sum(axis=1)
 
 
-def diagnose_head(q, k, v, perm, C: int, K: int, scale: float) -> dict:
+def diagnose_groups(q, k, v, groups: Sequence[np.ndarray], Ks: Sequence[int], scale: float) -> dict:
     """Recall and output error of the four selectors for one head.
 
-    q: [Nq, D]; k, v: [N, D]; perm: the query grouping (group g =
-    perm[g*C:(g+1)*C]);
-    K: keys per query block (a multiple of KV_BLOCK for the block selectors).
-    Returns {selector: {"recall": ..., "rel_l1": ...}}.
+    q: [Nq, D]; k, v: [N, D]; groups: the query blocks (arrays of query rows
+    that together cover every query once, any sizes); Ks: budgets (keys per
+    query block or per query; a multiple of KV_BLOCK for the block selectors).
+    Returns {K: {selector: {"recall": ..., "rel_l1": ...}}}.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     Nq, N = q.shape[0], k.shape[0]
     o_dense, lse = dense_attention(q, k, v, scale)
-    nblk = max(1, K // KV_BLOCK)
     kbar = np.stack([k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].mean(axis=0)
                      for b in range(-(-N // KV_BLOCK))])
-    rec = {s: 0.0 for s in SELECTORS}
-    err = {s: 0.0 for s in SELECTORS}
-    for rows in groups_from_perm(perm, C):
+    rec = {K: {s: 0.0 for s in SELECTORS} for K in Ks}
+    err = {K: {s: 0.0 for s in SELECTORS} for K in Ks}
+    for rows in groups:
+        rows = np.asarray(rows)
+        if rows.size == 0:
+            continue
         s = scale * (q[rows] @ k.T)
         p = np.exp(s - lse[rows][:, None])                 # exact probabilities [n, N]
         mass = p.sum(axis=0)                               # group mass per key
-        sets = {
-            "mean_pooled_block": _block_keys(_top_ids(scale * (kbar @ q[rows].mean(axis=0)), nblk), N),
-            "block_oracle": _block_keys(_top_ids(block_sums(mass, N), nblk), N),
-            "token_oracle": _top_ids(mass, K),
-        }
-        for name, ids in sets.items():
-            ps = p[:, ids]
-            kept = ps.sum(axis=1)
-            rec[name] += kept.sum()
-            o = (ps @ v[ids]) / kept[:, None]
-            err[name] += np.abs(o - o_dense[rows]).sum()
-        # per-query oracle: every row its own K largest probabilities (a tie at
-        # the K-th value may be broken either way: the kept mass is the same)
-        if K >= N:
-            pm = p
-        else:
-            top = np.argpartition(-p, K - 1, axis=1)[:, :K]
-            pm = np.zeros_like(p)
-            np.put_along_axis(pm, top, np.take_along_axis(p, top, axis=1), axis=1)
-        kept = pm.sum(axis=1)
-        rec["per_query_oracle"] += kept.sum()
-        err["per_query_oracle"] += np.abs((pm @ v) / kept[:, None] - o_dense[rows]).sum()
+        pooled = scale * (kbar @ q[rows].mean(axis=0))     # mean-pooled block scores
+        bmass = block_sums(mass, N)
+        order = None
+        for K in Ks:
+            nblk = max(1, K // KV_BLOCK)
+            sets = {
+                "mean_pooled_block": _block_keys(_top_ids(pooled, nblk), N),
+                "block_oracle": _block_keys(_top_ids(bmass, nblk), N),
+                "token_oracle": _top_ids(mass, K),
+            }
+            for name, ids in sets.items():
+                ps = p[:, ids]
+                kept = ps.sum(axis=1)
+                rec[K][name] += kept.sum()
+                err[K][name] += np.abs((ps @ v[ids]) / kept[:, None] - o_dense[rows]).sum()
+            # per-query oracle: every row its own K largest probabilities (a tie
+            # at the K-th value may be broken either way: the kept mass is the same)
+            if K >= N:
+                pm = p
+            else:
+                if order is None:
+                    order = np.argsort(-p, axis=1, kind="stable")
+                top = order[:, :K]
+                pm = np.zeros_like(p)
+                np.put_along_axis(pm, top, np.take_along_axis(p, top, axis=1), axis=1)
+            kept = pm.sum(axis=1)
+            rec[K]["per_query_oracle"] += kept.sum()
+            err[K]["per_query_oracle"] += np.abs((pm @ v) / kept[:, None] - o_dense[rows]).sum()
     total = np.abs(o_dense).sum()
-    return {s: {"recall": rec[s] / Nq, "rel_l1": err[s] / total} for s in SELECTORS}
+    return {K: {s: {"recall": rec[K][s] / Nq, "rel_l1": err[K][s] / total} for s in SELECTORS}
+            for K in Ks}
+
+
+def diagnose_head(q, k, v, perm, C: int, K: int, scale: float) -> dict:
+    """diagnose_groups for the query blocks perm[g*C:(g+1)*C] and one budget K.
+
+    Returns {selector: {"recall": ..., "rel_l1": ...}}.
+    """
+    return diagnose_groups(q, k, v, groups_from_perm(perm, C), [K], scale)[K]
+
+
+def kmeans(x, init, rounds: int):
+    """Lloyd's k-means (reading D6) from the given initial centres.
+
+    x: [n, D] points; init: [k, D] initial centres; rounds: assignment/update
+    rounds.  Returns (labels [n] int, centres [k, D], inertia per round [rounds]).
+    """
+    x = _f64(x)
+    c = _f64(init).copy()
+    k = c.shape[0]
+    xx = (x * x).sum(axis=1)
+    inertia = []
+    labels = np.zeros(x.shape[0], dtype=np.int64)
+    for _ in range(rounds):
+        d = xx[:, None] - 2.0 * (x @ c.T) + (c * c).sum(axis=1)[None, :]
+        labels = np.argmin(d, axis=1)                      # first minimum: smaller centre id
+        inertia.append(float(((x - c[labels]) ** 2).sum()))
+        counts = np.bincount(labels, minlength=k)
+        sums = np.zeros_like(c)
+        np.add.at(sums, labels, x)
+        nz = counts > 0
+        c[nz] = sums[nz] / counts[nz][:, None]
+    return labels, c, np.array(inertia)
+
+
+def cluster_groups(labels, k: int) -> list[np.ndarray]:
+    """Member rows of each of the k clusters (ascending), empty ones included."""
+    order = np.argsort(labels, kind="stable")
+    bounds = np.searchsorted(labels[order], np.arange(k + 1))
+    return [order[bounds[j]:bounds[j + 1]] for j in range(k)]
+
+
+def alignment_inflation(sizes, tile: int) -> float:
+    """Rows computed when every cluster is padded to whole tiles, over the real
+    rows (reading D7): sum ceil(n/tile)*tile / sum n."""
+    sizes = np.asarray(sizes, dtype=np.int64)
+    return float((-(-sizes // tile) * tile).sum() / sizes.sum())

@@ -6,7 +6,10 @@ the best block set, the best block set at least that of any block set), the
 full budget keeps everything, the block oracle is checked against brute force
 over all block subsets, and a hand-built case shows mean pooling missing a
 high-mass token that the token oracle keeps (recall and output error in
-closed form).
+closed form).  k-means is pinned to scikit-learn's Lloyd implementation from
+the same initial centres, to planted well-separated clusters and their means,
+to the monotone inertia of Lloyd's algorithm and to its tie and empty-cluster
+rules; the alignment inflation to closed forms.
 """
 import itertools
 import math
@@ -105,3 +108,69 @@ def test_mean_pooling_misses_a_high_mass_token():
     assert abs(r["mean_pooled_block"]["recall"] - 64 / Z) < 1e-12
     assert abs(r["block_oracle"]["recall"] - (math.exp(4) + 63 * math.exp(-0.5)) / Z) < 1e-12
     assert abs(r["token_oracle"]["recall"] - (math.exp(4) + 63) / Z) < 1e-12
+
+
+# ---- k-means grouping and alignment inflation -----------------------------
+
+def test_kmeans_matches_scikit_learn_lloyd():
+    # same initial centres, run to convergence: identical centres and labels
+    from sklearn.cluster import KMeans
+    r = np.random.default_rng(7)
+    x = np.concatenate([r.normal(m, 1.0, (n, 5)) for m, n in ((0, 80), (4, 50), (-4, 70), (8, 30))])
+    init = x[r.choice(len(x), 6, replace=False)]
+    lab, cen, _ = dg.kmeans(x, init, 100)
+    km = KMeans(n_clusters=6, init=init, n_init=1, max_iter=100, tol=0.0, algorithm="lloyd").fit(x)
+    np.testing.assert_allclose(cen, km.cluster_centers_, rtol=0, atol=1e-10)
+    np.testing.assert_array_equal(lab, km.labels_)
+
+
+def test_kmeans_recovers_planted_clusters_and_their_means():
+    r = np.random.default_rng(3)
+    sizes = (40, 17, 90, 5)
+    centres = np.array([[0, 0, 0], [50, 0, 0], [0, 50, 0], [0, 0, 50]], dtype=float)
+    x = np.concatenate([c + r.uniform(-1, 1, (n, 3)) for c, n in zip(centres, sizes)])
+    truth = np.repeat(np.arange(4), sizes)
+    init = x[[0, 40, 57, 147]]                     # one member of each cluster
+    lab, cen, inertia = dg.kmeans(x, init, 3)
+    np.testing.assert_array_equal(lab, truth)
+    for j in range(4):
+        np.testing.assert_allclose(cen[j], x[truth == j].mean(axis=0), rtol=0, atol=1e-12)
+    groups = dg.cluster_groups(lab, 4)
+    assert [g.size for g in groups] == list(sizes)
+    assert dg.alignment_inflation([g.size for g in groups], 64) == pytest.approx((64 + 64 + 128 + 64) / 152)
+
+
+def test_kmeans_inertia_never_rises_and_ties_go_to_the_smaller_centre():
+    r = np.random.default_rng(11)
+    x = r.standard_normal((300, 4))
+    _, _, inertia = dg.kmeans(x, x[:12], 25)
+    assert np.all(np.diff(inertia) <= 1e-9)
+    lab, _, _ = dg.kmeans(np.zeros((1, 2)), np.array([[-1.0, 0.0], [1.0, 0.0]]), 1)
+    assert lab[0] == 0
+    # an empty cluster keeps its centre
+    lab, cen, _ = dg.kmeans(np.array([[0.0], [0.1]]), np.array([[0.0], [100.0]]), 2)
+    assert list(lab) == [0, 0] and cen[1, 0] == 100.0
+
+
+@pytest.mark.parametrize("sizes,tile,want", [([64, 64], 64, 1.0), ([65, 63], 64, 1.5),
+                                              ([1] * 10, 8, 8.0), ([128, 1, 127], 128, 384 / 256)])
+def test_alignment_inflation_closed_forms(sizes, tile, want):
+    assert dg.alignment_inflation(sizes, tile) == pytest.approx(want, rel=1e-15)
+
+
+def test_budgets_in_one_call_equal_separate_calls_and_kmeans_groups_keep_the_ordering():
+    N, C = 384, 64
+    q, k, v = _head(N, 16, 21)
+    r = np.random.default_rng(22)
+    lab, _, _ = dg.kmeans(q, q[r.choice(N, N // C, replace=False)], 10)
+    groups = [g for g in dg.cluster_groups(lab, N // C) if g.size]
+    both = dg.diagnose_groups(q, k, v, groups, [64, 128], 0.3)
+    for K in (64, 128):
+        one = dg.diagnose_groups(q, k, v, groups, [K], 0.3)[K]
+        for s in dg.SELECTORS:
+            assert both[K][s]["recall"] == pytest.approx(one[s]["recall"], rel=1e-13)
+            assert both[K][s]["rel_l1"] == pytest.approx(one[s]["rel_l1"], rel=1e-13)
+        r_ = both[K]
+        assert r_["per_query_oracle"]["recall"] >= r_["token_oracle"]["recall"] - 1e-12
+        assert r_["token_oracle"]["recall"] >= r_["block_oracle"]["recall"] - 1e-12
+        assert r_["block_oracle"]["recall"] >= r_["mean_pooled_block"]["recall"] - 1e-12
