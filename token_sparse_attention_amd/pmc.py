@@ -2,6 +2,7 @@
 
     python -m token_sparse_attention_amd.pmc FETCH_DIR WRITE_DIR OUT.json [--workload large]
     python -m token_sparse_attention_amd.pmc --util UTIL_DIR OUT.json
+    python -m token_sparse_attention_amd.pmc --l2 L2_DIR OUT.json
 
 FETCH_DIR and WRITE_DIR are the output directories of two runs of
 
@@ -24,6 +25,13 @@ per kernel: the average shader clock over the dispatch (GRBM_GUI_ACTIVE, summed
 over the 8 XCDs, divided by the dispatch time), the share of SIMD cycles in
 which the MFMA unit was busy, and the share in which a plain VALU
 instruction issued while it was (co-execution).
+
+--l2 summarises one run of
+
+    rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum -d L2_DIR -o pmc --output-format csv -- python3 bench.py ...
+
+per kernel: L2 hits and misses per dispatch and the hit rate (a miss is a
+128-byte line requested from the fabric: MALL or HBM).
 """
 from __future__ import annotations
 
@@ -115,7 +123,26 @@ def utilisation(util_dir: str) -> dict:
     return {"source_hash": source_hash(), "kernels": out}
 
 
+def l2(l2_dir: str) -> dict:
+    hits = _per_kernel(l2_dir, "TCC_HIT_sum")
+    miss = _per_kernel(l2_dir, "TCC_MISS_sum")
+    out = {}
+    for k in sorted(set(hits) & set(miss)):
+        tot = hits[k] + miss[k]
+        out[k] = {"hits": hits[k], "misses": miss[k], "hit_rate": hits[k] / tot if tot else None,
+                  "miss_bytes": 128.0 * miss[k]}
+    return {"source_hash": source_hash(), "kernels": out}
+
+
 def main(argv):
+    if argv and argv[0] == "--l2":
+        out = l2(argv[1])
+        with open(argv[2], "w") as f:
+            json.dump(out, f, indent=1)
+        for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["misses"]):
+            print(f"{k:48s} hit rate {100 * (v['hit_rate'] or 0):5.1f}%  misses {v['misses']:.3e}"
+                  f"  ({v['miss_bytes'] / 1e9:.2f} GB of lines)")
+        return 0
     if argv and argv[0] == "--util":
         out = utilisation(argv[1])
         with open(argv[2], "w") as f:
