@@ -4,7 +4,8 @@ Group sizes must match exactly (a permutation, groups of C, one short last
 group by construction of perm), and the within-group variance W of the GPU's
 grouping must be within 1% of the oracle's (exact eigenvectors).  Closed-form
 cases (collinear queries, identical queries, separated clusters) must match
-exactly.
+exactly, and collinear queries with repeated values at ragged sizes (a short
+remainder group, one group, N < C) must give the oracle's groups exactly.
 """
 import numpy as np
 import pytest
@@ -86,3 +87,21 @@ def test_deterministic(mcs):
     a = mcs.group(dq, 64).cpu().numpy()
     b = mcs.group(dq, 64).cpu().numpy()
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("N,C", [(337, 64), (1000, 128), (129, 128), (50, 64), (64, 64), (4097, 64)])
+def test_collinear_ragged_matches_oracle_exactly(mcs, N, C):
+    # queries on one axis with small-integer coordinates (exact in bf16, with
+    # repeats): the principal direction is that axis at every node, so the
+    # grouping is fixed by the split rule (rank C*floor(g/2) of the ordering by
+    # projection, then query id) and must equal the oracle's group by group,
+    # including the short remainder group and the single-group cases
+    D = 64
+    t = (np.random.default_rng(N).permutation(N) % 97).astype(np.float32)
+    q = np.zeros((1, 1, N, D), dtype=np.float32)
+    q[0, 0, :, 5] = t - 40.0
+    bits = synth.to_bf16_bits(q)
+    perm = mcs.group(to_dev_bf16(bits), C).cpu().numpy()[0, 0]
+    assert_perm(perm[None])
+    ref = oracle.pddp(synth.to_f64(bits)[0, 0], C)
+    assert [sorted(g) for g in _groups(perm, C)] == [sorted(g) for g in _groups(ref, C)]
