@@ -146,3 +146,14 @@ def test_group_workspace_grows_with_partials(lib):
     assert small >= 8 * 1024
     large = lib.mcs_group_workspace(Dims(1, 40, 75600, 128), 128)
     assert large > 8 * 40 * 75600 + 40 * 37 * (128 * 128 + 128) * 4
+
+
+def test_layout_helpers_round_trip():
+    import torch
+    from token_sparse_attention_amd import binding
+    x = torch.arange(2 * 5 * 3 * 4, dtype=torch.float32).reshape(2, 5, 3, 4)      # [B, N, H, D]
+    y = binding.heads_major(x)
+    assert y.shape == (2, 3, 5, 4) and y.is_contiguous()
+    assert torch.equal(y[1, 2, 4], x[1, 4, 2])
+    z = binding.tokens_major(y)
+    assert z.is_contiguous() and torch.equal(z, x)

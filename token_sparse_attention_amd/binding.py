@@ -108,6 +108,22 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
+def heads_major(x: torch.Tensor) -> torch.Tensor:
+    """[B, N, H, D] (the token-major layout of a transformer's projections) ->
+    contiguous [B, H, N, D], the layout every call takes.  A torch copy, made
+    once per tensor before the calls (outside the attention path)."""
+    if x.dim() != 4:
+        raise ValueError("expected a [B, N, H, D] tensor")
+    return x.transpose(1, 2).contiguous()
+
+
+def tokens_major(x: torch.Tensor) -> torch.Tensor:
+    """Inverse of heads_major: [B, H, N, D] -> contiguous [B, N, H, D]."""
+    if x.dim() != 4:
+        raise ValueError("expected a [B, H, N, D] tensor")
+    return x.transpose(1, 2).contiguous()
+
+
 def _qkv(q, k, v=None):
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
