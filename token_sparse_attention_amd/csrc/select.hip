@@ -39,10 +39,6 @@ struct MassParams {
   float sl2;
 };
 
-#ifndef MCS_MASS_VALU
-#define MCS_MASS_VALU 3          // exponential-side VALU instructions after each MFMA of the next block
-#endif
-
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   constexpr int CH = D / 8;                 // 16-byte chunks per row
@@ -138,9 +134,10 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
 
   // Step t: wait for K_t, barrier (K_{t-1} and the partial masses of tile
   // t-1 are then free / complete), gather K_{t+1} into the other buffer,
-  // store tile t-1's mass, then S = Q K_t^T with the exponentials of the
-  // first 32-key block interleaved with the MFMAs of the second.  The loop is
-  // unrolled by the two buffers so all LDS offsets are immediates.
+  // store tile t-1's mass, then S = Q K_t^T with the MFMA chains of the two
+  // 32-key blocks alternating (independent accumulators back to back), then
+  // the exponentials; the other waves on the SIMD fill the MFMA gaps.  The
+  // loop is unrolled by the two buffers so all LDS offsets are immediates.
   const int ntiles = (p.N + MKT - 1) / MKT;
   auto step = [&](auto buf_c, int t) {
     constexpr int BUF = decltype(buf_c)::value;
@@ -151,30 +148,15 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
     const char* kt = lbase + BUF * TILE_BYTES;
     f32x16_t acc0 = zero16(), acc1 = zero16();
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+    for (int ks = 0; ks < KSTEPS; ++ks) {
       acc0 = mfma32x32x16(qf[ks], as_bf16x8(*reinterpret_cast<const u32x4_t*>(kt + koff[ks])), acc0);
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
       acc1 = mfma32x32x16(qf[ks], as_bf16x8(*reinterpret_cast<const u32x4_t*>(kt + 32 * ROWB + koff[ks])), acc1);
+    }
     const float m0 = block_mass(acc0);
     const float m1 = block_mass(acc1);
     if (hh == 0) {
       red[BUF][w][lq] = m0;
       red[BUF][w][32 + lq] = m1;
-    }
-    // K fragment reads two MFMAs ahead; block 0's exponentials ride on
-    // block 1's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + 2 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, MCS_MASS_VALU, 0);
     }
   };
   issue(0, 0);
