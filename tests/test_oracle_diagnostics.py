@@ -174,3 +174,25 @@ def test_budgets_in_one_call_equal_separate_calls_and_kmeans_groups_keep_the_ord
         assert r_["per_query_oracle"]["recall"] >= r_["token_oracle"]["recall"] - 1e-12
         assert r_["token_oracle"]["recall"] >= r_["block_oracle"]["recall"] - 1e-12
         assert r_["block_oracle"]["recall"] >= r_["mean_pooled_block"]["recall"] - 1e-12
+
+
+def test_per_query_oracle_equals_brute_force_masking():
+    # every row keeps its K largest probabilities; recall and output error
+    # recomputed here from a dense mask and a plain product, several budgets
+    N, C = 300, 64
+    q, k, v = _head(N, 8, 31)
+    scale = 0.5
+    groups = dg.groups_from_perm(np.random.default_rng(32).permutation(N), C)
+    Ks = [1, 37, 128, 299, 300]
+    got = dg.diagnose_groups(q, k, v, groups, Ks, scale)
+    o, lse = oracle.dense_attention(q, k, v, scale)
+    p = np.exp(scale * q @ k.T - lse[:, None])
+    for K in Ks:
+        keep = np.zeros_like(p, dtype=bool)
+        for i in range(N):
+            keep[i, np.argsort(-p[i], kind="stable")[:K]] = True
+        pm = np.where(keep, p, 0.0)
+        kept = pm.sum(axis=1)
+        assert got[K]["per_query_oracle"]["recall"] == pytest.approx(kept.mean(), rel=1e-12)
+        err = np.abs(pm @ v / kept[:, None] - o).sum() / np.abs(o).sum()
+        assert got[K]["per_query_oracle"]["rel_l1"] == pytest.approx(err, rel=1e-10, abs=1e-14)
