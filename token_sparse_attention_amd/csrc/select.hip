@@ -15,10 +15,13 @@
 // combine through LDS in a fixed order.  One fp32 mass row of N values per
 // group goes to the workspace.
 //
-// topk_kernel: one 1024-thread workgroup per mass row: 4-pass radix select of
-// the K-th largest value (8 bits per pass, per-wave LDS histograms), then an
+// topk_reg_kernel: one 1024-thread workgroup per mass row of up to 81920
+// values, held on chip (registers and LDS): radix select of the K-th largest
+// value in passes of 12, 12 and 8 bits over one shared histogram, then an
 // order-preserving compaction that writes the chosen ids in ascending order,
-// equal values going to the smaller id.
+// equal values going to the smaller id.  topk_kernel: the same selection for
+// longer rows, streaming the row from memory (four 8-bit passes with per-wave
+// LDS histograms, then the compaction).
 #include <type_traits>
 
 #include "mcs_common.h"

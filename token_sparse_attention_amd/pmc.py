@@ -40,19 +40,28 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed (the code)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources the counters describe."""
+    """Hash of the code of the HIP sources the counters describe (comments and
+    whitespace do not count, so editing a comment keeps the counters valid)."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
-        with open(f, "rb") as fh:
+        with open(f, encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
