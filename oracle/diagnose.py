@@ -1,13 +1,15 @@
 """Recall, output error and k-means alignment inflation on synthetic heads.
 
-    python -m oracle.diagnose [--workloads tiny small asset3d] [--heads 1] [--rounds 20]
+    python -m oracle.diagnose [--workloads tiny small asset3d] [--heads 1] [--rounds 20] [--groups 48]
 
 Test-infrastructure script (it uses only ``oracle`` and the seeded input
 generators): for one or more heads of each workload, every selector of
 ``oracle.diagnostics`` at densities 0.1, 0.2 and 0.3 (K = 128*floor(s*N/128)),
 with three query groupings: C consecutive queries, PDDP groups, and k-means
 clusters (ceil(N/C) of them, Lloyd's algorithm from distinct queries drawn
-with a seeded generator).  A second table gives the alignment inflation of
+with a seeded generator); recall and output error are means over the queries
+of a seeded sample of --groups query blocks per grouping (all of them when a
+grouping has fewer).  A second table gives the alignment inflation of
 k-means (query clusters padded to C; key clusters, ceil(N/64) of them, padded
 to 64) and the recall k-means grouping keeps when its inflated compute is held
 to the nominal budget (token oracle with floor(K/f_tok) keys, block oracle
@@ -46,6 +48,7 @@ def main(argv=None):
     ap.add_argument("--workloads", nargs="+", default=["tiny", "small", "asset3d"])
     ap.add_argument("--heads", type=int, default=1)
     ap.add_argument("--rounds", type=int, default=20, help="k-means rounds")
+    ap.add_argument("--groups", type=int, default=48, help="query blocks scored per grouping")
     args = ap.parse_args(argv)
     main_rows, km_rows = [], []
     for name in args.workloads:
@@ -68,13 +71,20 @@ def main(argv=None):
             f_blk = f_tok * f_key
             matched_tok = {K: int(K / f_tok) for K in nominal}
             matched_blk = {K: 64 * int(K / f_blk / 64) for K in nominal}
+            def sample(groups):
+                groups = [g for g in groups if g.size]
+                if len(groups) <= args.groups:
+                    return groups
+                return [groups[i] for i in np.sort(rng.choice(len(groups), args.groups, replace=False))]
+
             res = {
-                "contiguous": dg.diagnose_groups(q, k, v, dg.groups_from_perm(np.arange(w.N), w.C), nominal, scale),
-                "PDDP": dg.diagnose_groups(q, k, v, dg.groups_from_perm(oracle.pddp(q, w.C), w.C), nominal, scale),
+                "contiguous": dg.diagnose_groups(q, k, v, sample(dg.groups_from_perm(np.arange(w.N), w.C)),
+                                                 nominal, scale),
+                "PDDP": dg.diagnose_groups(q, k, v, sample(dg.groups_from_perm(oracle.pddp(q, w.C), w.C)),
+                                           nominal, scale),
             }
             extra = sorted(set(matched_tok.values()) | {m for m in matched_blk.values() if m > 0})
-            res["k-means"] = dg.diagnose_groups(q, k, v, [g for g in qgroups if g.size],
-                                                sorted(set(nominal) | set(extra)), scale)
+            res["k-means"] = dg.diagnose_groups(q, k, v, sample(qgroups), sorted(set(nominal) | set(extra)), scale)
             for gname, r in res.items():
                 for sel in dg.SELECTORS:
                     rec = " | ".join(_cell(r, Ks[s], sel, "recall") for s in DENS)

@@ -87,22 +87,26 @@ def block_sums(x: np.ndarray, N: int) -> np.ndarray:
 def diagnose_groups(q, k, v, groups: Sequence[np.ndarray], Ks: Sequence[int], scale: float) -> dict:
     """Recall and output error of the four selectors for one head.
 
-    q: [Nq, D]; k, v: [N, D]; groups: the query blocks (arrays of query rows
-    that together cover every query once, any sizes); Ks: budgets (keys per
-    query block or per query; a multiple of KV_BLOCK for the block selectors).
-    Returns {K: {selector: {"recall": ..., "rel_l1": ...}}}.
+    q: [Nq, D]; k, v: [N, D]; groups: the query blocks to score (disjoint
+    arrays of query rows, any sizes; the statistics are over the queries they
+    hold, so a sample of a grouping's blocks gives a sample estimate); Ks:
+    budgets (keys per query block or per query; a multiple of KV_BLOCK for the
+    block selectors).  Returns {K: {selector: {"recall": ..., "rel_l1": ...}}}.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    Nq, N = q.shape[0], k.shape[0]
-    o_dense, lse = dense_attention(q, k, v, scale)
+    N = k.shape[0]
+    groups = [np.asarray(g) for g in groups if len(g)]
+    held = np.concatenate(groups)
+    Nq = held.size
+    o_held, lse_held = dense_attention(q[held], k, v, scale)
+    o_dense = np.zeros((q.shape[0], v.shape[1]))
+    lse = np.zeros(q.shape[0])
+    o_dense[held], lse[held] = o_held, lse_held
     kbar = np.stack([k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].mean(axis=0)
                      for b in range(-(-N // KV_BLOCK))])
     rec = {K: {s: 0.0 for s in SELECTORS} for K in Ks}
     err = {K: {s: 0.0 for s in SELECTORS} for K in Ks}
     for rows in groups:
-        rows = np.asarray(rows)
-        if rows.size == 0:
-            continue
         s = scale * (q[rows] @ k.T)
         p = np.exp(s - lse[rows][:, None])                 # exact probabilities [n, N]
         mass = p.sum(axis=0)                               # group mass per key
@@ -120,28 +124,27 @@ def diagnose_groups(q, k, v, groups: Sequence[np.ndarray], Ks: Sequence[int], sc
                 kept = ps.sum(axis=1)
                 rec[K][name] += kept.sum()
                 err[K][name] += np.abs((ps @ v[ids]) / kept[:, None] - o_dense[rows]).sum()
-        # per-query oracle: every row keeps its own K largest probabilities (a
-        # tie at the K-th value may be broken either way: the kept mass is the
-        # same).  Each row is sorted once; kept mass and sum_j P_ij v_j are
-        # accumulated over the sorted keys segment by segment between
-        # consecutive budgets, so every budget costs one pass in total.
+        # per-query oracle: every row keeps its own K largest probabilities, a
+        # tie at the K-th value going to the smaller key id.  One partition
+        # per row gives the K-th largest value t of every budget; the kept set
+        # is {p > t} plus the first (K - #{p > t}) keys with p == t.
         budgets = sorted(set(min(K, N) for K in Ks))
-        kmax = budgets[-1]
-        for r0 in range(0, rows.size, 32):
-            pr = p[r0:r0 + 32]
-            order = np.argsort(-pr, axis=1, kind="stable")[:, :kmax]
-            ps = np.take_along_axis(pr, order, axis=1)                    # [r, kmax], descending
-            starts = [0] + budgets[:-1]
-            seg_p = np.add.reduceat(ps, starts, axis=1)                   # [r, nb]
-            seg_o = np.add.reduceat(ps[:, :, None] * v[order], starts, axis=1)   # [r, nb, D]
-            kept_b = np.cumsum(seg_p, axis=1)
-            o_b = np.cumsum(seg_o, axis=1) / kept_b[:, :, None]
-            ref = o_dense[rows[r0:r0 + 32]]
-            for K in Ks:
-                b = budgets.index(min(K, N))
-                rec[K]["per_query_oracle"] += kept_b[:, b].sum()
-                err[K]["per_query_oracle"] += np.abs(o_b[:, b] - ref).sum()
-    total = np.abs(o_dense).sum()
+        for r0 in range(0, rows.size, 64):
+            pr = p[r0:r0 + 64]
+            ref = o_dense[rows[r0:r0 + 64]]
+            part = -np.partition(-pr, [K - 1 for K in budgets], axis=1)
+            for K in budgets:
+                t = part[:, K - 1][:, None]
+                gt = pr > t
+                eq = pr == t
+                need = K - gt.sum(axis=1, keepdims=True)
+                keep = gt | (eq & (np.cumsum(eq, axis=1) <= need))
+                pm = np.where(keep, pr, 0.0)
+                kept = pm.sum(axis=1)
+                for Kq in (Kq for Kq in Ks if min(Kq, N) == K):
+                    rec[Kq]["per_query_oracle"] += kept.sum()
+                    err[Kq]["per_query_oracle"] += np.abs((pm @ v) / kept[:, None] - ref).sum()
+    total = np.abs(o_held).sum()
     return {K: {s: {"recall": rec[K][s] / Nq, "rel_l1": err[K][s] / total} for s in SELECTORS}
             for K in Ks}
 

@@ -196,3 +196,15 @@ def test_per_query_oracle_equals_brute_force_masking():
         assert got[K]["per_query_oracle"]["recall"] == pytest.approx(kept.mean(), rel=1e-12)
         err = np.abs(pm @ v / kept[:, None] - o).sum() / np.abs(o).sum()
         assert got[K]["per_query_oracle"]["rel_l1"] == pytest.approx(err, rel=1e-10, abs=1e-14)
+
+
+def test_scoring_a_sample_of_groups_averages_over_their_queries():
+    # recall is a mean over the queries the given groups hold: scoring the
+    # groups one at a time and weighting by group size gives the full result
+    N, C = 320, 64
+    q, k, v = _head(N, 8, 41)
+    groups = dg.groups_from_perm(np.random.default_rng(42).permutation(N), C)
+    full = dg.diagnose_groups(q, k, v, groups, [64], 0.4)[64]
+    for s in dg.SELECTORS:
+        parts = [dg.diagnose_groups(q, k, v, [g], [64], 0.4)[64][s]["recall"] * len(g) for g in groups]
+        assert sum(parts) / N == pytest.approx(full[s]["recall"], rel=1e-12)
