@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--offload-layers", type=int, default=0,
                     help="time reuse steps over this many layers with the anchor cache resident vs offloaded")
+    ap.add_argument("--torch-sdpa", action="store_true",
+                    help="also time torch's scaled_dot_product_attention (flash backend) on the dense shape")
     ap.add_argument("--all-workloads", action="store_true",
                     help="every workload and density (one JSON line each) instead of the headline one")
     return ap.parse_args()
@@ -137,6 +139,28 @@ def measured_util(workload: str, kernel_prefix: str):
         if name.startswith(kernel_prefix):
             return v
     return None
+
+
+def torch_sdpa_ms(q, k, v, reps: int):
+    """Context for the dense baseline: torch's scaled_dot_product_attention on
+    the same bf16 tensors, restricted to its flash backend (an unsupported case
+    raises instead of falling back to the bf16 math path).  Returns the mean
+    ms, or the error text."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            f = torch.nn.functional.scaled_dot_product_attention
+            f(q, k, v)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            for i in range(reps):
+                ev[i].record()
+                f(q, k, v)
+            ev[reps].record()
+            torch.cuda.synchronize()
+        return round(float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), 4)
+    except Exception as ex:  # no flash backend for this device or shape
+        return f"unavailable: {str(ex)[:160]}"
 
 
 def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
@@ -228,6 +252,7 @@ def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     dense_nolse_ms = float(np.mean([e0[i].elapsed_time(e0[i + 1]) for i in range(reps)]))
     speedup = dense_nolse_ms / ms["sparse_reuse"]
+    torch_sdpa = torch_sdpa_ms(q0, k0, v0, reps) if args.torch_sdpa else None
 
     sparse_flops = accounting.sparse_flops(B, H, N, K, D)
     dense_flops = accounting.dense_flops(B, H, N, D)
@@ -264,6 +289,7 @@ def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
                            "frac": round(dense_flops / (ms["dense_lse"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "stage_ms": {k: round(v, 4) for k, v in ms.items()},
         "dense_nolse_ms": round(dense_nolse_ms, 4),
+        "torch_sdpa_flash_ms": torch_sdpa,
         "speedup_vs_dense_with_lse": round(ms["dense_lse"] / ms["sparse_reuse"], 4),
         "ideal_speedup": round(N / K, 4),
         "efficiency_vs_ideal": round(speedup * K / N, 4),
