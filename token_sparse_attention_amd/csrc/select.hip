@@ -17,7 +17,8 @@
 //
 // topk_reg_kernel: one 1024-thread workgroup per mass row of up to 81920
 // values, held on chip (registers and LDS): radix select of the K-th largest
-// value in passes of 12, 12 and 8 bits over one shared histogram, then an
+// value in passes of 12, 12 and 8 bits over one shared histogram (the finer
+// passes over the keys that share the first digit, gathered into LDS), then an
 // order-preserving compaction that writes the chosen ids in ascending order,
 // equal values going to the smaller id.  topk_kernel: the same selection for
 // longer rows, streaming the row from memory (four 8-bit passes with per-wave
@@ -214,22 +215,11 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(const float* __restrict__
   });
 }
 
-// Adds one to hist[bin] for every active lane.  Lanes that share a bin with
-// the lowest pending lane are counted with one atomic for the lot (done twice,
-// which takes the bins most lanes fall in: mass values mostly share their
-// leading key bits); the rest add their own.
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t bin, int lane) {
-  uint64_t pend = __ballot(active);
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    if (pend == 0) break;
-    const int leader = __ffsll((unsigned long long)pend) - 1;
-    const uint32_t lb = __shfl(bin, leader);
-    const uint64_t same = __ballot(active && bin == lb) & pend;
-    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
-    pend &= ~same;
-  }
-  if ((pend >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+// Adds one to hist[bin] for every active lane (one LDS atomic per lane).
+// Grouping the lanes of a wave that share a bin (a leader per bin, one atomic
+// for the lot) was measured slower on the mass rows than the plain atomics.
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t bin) {
+  if (active) atomicAdd(&hist[bin], 1u);
 }
 
 // The same selection with the whole row held on chip (element i of the row in
@@ -238,20 +228,28 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t b
 // once per radix pass and once more for the compaction.  Rows of up to
 // TOPK_NT * SLOTS values.  Slots past the row end hold the largest key (that
 // of a zero score): they rank after every element of the row, so they never
-// change the K-th key (K <= n); the compaction skips them.  The compaction
-// counts, per round of TOPK_NT positions and per wave, the keys below and
-// equal to the threshold, scans those counts once in position order, and then
-// places every chosen id without further synchronisation.
+// change the K-th key (K <= n); the compaction skips them.  Only the keys that
+// share the first 12-bit digit with the K-th key matter to the two finer
+// passes; when they fit (up to CAND_CAP) they are gathered into LDS first, so
+// those passes cost no more than their number.  The compaction counts, per
+// round of TOPK_NT positions and per wave, the keys below and equal to the
+// threshold, scans those counts once in position order, and then places every
+// chosen id without further synchronisation.
 template <int SLOTS, int RSLOTS>
 __global__ __launch_bounds__(TOPK_NT) void topk_reg_kernel(const float* __restrict__ scores,
                                                           int32_t* __restrict__ idx, int n, int K) {
   constexpr int NWV = TOPK_NT / 64;
   constexpr int HBINS = 4096;
+  constexpr int CAND_CAP = 6080;             // candidate keys (the LDS left beside the row)
+  static_assert(CAND_CAP >= 2 * SLOTS * NWV, "the count arrays live in the candidate area");
   __shared__ uint32_t hist[HBINS];
   __shared__ uint32_t wtot[NWV];
-  __shared__ uint32_t sel_digit, sel_below;
+  __shared__ uint32_t sel_digit, sel_below, ncand;
   __shared__ uint32_t kl[SLOTS - RSLOTS][TOPK_NT];
-  __shared__ uint32_t cnt[2][SLOTS * NWV];   // [lt | eq][round * NWV + wave], scanned in place
+  // candidate keys during the finer passes, then [lt | eq][round * NWV + wave]
+  // counts of the compaction, scanned in place
+  __shared__ uint32_t cand_area[CAND_CAP];
+  uint32_t (*cnt)[SLOTS * NWV] = reinterpret_cast<uint32_t (*)[SLOTS * NWV]>(cand_area);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const size_t row = blockIdx.x;
   const uint32_t* __restrict__ x = reinterpret_cast<const uint32_t*>(scores) + row * (size_t)n;
@@ -259,40 +257,26 @@ __global__ __launch_bounds__(TOPK_NT) void topk_reg_kernel(const float* __restri
   const int nslots = (n + TOPK_NT - 1) / TOPK_NT;
   // larger score -> smaller key; -0.0 (and any negative, which is not allowed) -> as 0
   auto to_key = [](uint32_t u) -> uint32_t { return ~((u & 0x80000000u) ? 0u : u); };
+  // register slots first, so the first histogram pass can start on them while
   // the LDS slots arrive by DMA (raw score bits; reads past the row end give
-  // 0, a zero score), all in flight together with the register slots' loads
-  const __amdgpu_buffer_rsrc_t rrow = head_rsrc(x, (uint32_t)n * 4u);
-  for (int k = RSLOTS; k < nslots; ++k)
-    dma4(rrow, (uint32_t)(k * TOPK_NT + tid) * 4u, &kl[k - RSLOTS][w * 64]);
+  // 0, a zero score)
   uint32_t kv[RSLOTS];
 #pragma unroll
   for (int k = 0; k < RSLOTS; ++k) {
     const int i = k * TOPK_NT + tid;
     kv[k] = to_key(i < n ? x[i] : 0u);
   }
-  wait_vmem_all();
+  const __amdgpu_buffer_rsrc_t rrow = head_rsrc(x, (uint32_t)n * 4u);
+  for (int k = RSLOTS; k < nslots; ++k)
+    dma4(rrow, (uint32_t)(k * TOPK_NT + tid) * 4u, &kl[k - RSLOTS][w * 64]);
+  for (int i = tid; i < HBINS; i += TOPK_NT) hist[i] = 0u;
+  if (tid == 0) ncand = 0u;
   __syncthreads();
   auto lkey = [&](int k) -> uint32_t { return to_key(kl[k - RSLOTS][tid]); };
-  // radix select of the K-th smallest key in three passes of 12, 12 and 8
-  // bits over one shared histogram: after the first pass few keys still
-  // match the prefix, so the later passes cost little more than a compare
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = K;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const uint32_t dmask = pass == 2 ? 255u : 4095u;
-    for (int i = tid; i < HBINS; i += TOPK_NT) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < RSLOTS; ++k)
-      if (k < nslots) hist_add(hist, (kv[k] & pmask) == prefix, (kv[k] >> shift) & dmask, lane);
-#pragma unroll 2
-    for (int k = RSLOTS; k < nslots; ++k) {
-      const uint32_t key = lkey(k);
-      hist_add(hist, (key & pmask) == prefix, (key >> shift) & dmask, lane);
-    }
-    __syncthreads();
-    // the bin holding the remaining-th key: thread t owns bins 4t .. 4t+3
+
+  // the bin holding the remaining-th key of the histogram: thread t owns bins
+  // 4t .. 4t+3; sets sel_digit and sel_below (keys in smaller bins)
+  auto pick = [&](int remaining) {
     uint32_t c[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) c[q] = hist[4 * tid + q];
@@ -323,6 +307,71 @@ __global__ __launch_bounds__(TOPK_NT) void topk_reg_kernel(const float* __restri
       }
     }
     __syncthreads();
+  };
+
+  // radix select of the K-th smallest key in passes of 12, 12 and 8 bits.
+  // Pass 1 over the whole row: every key is active.
+#pragma unroll
+  for (int k = 0; k < RSLOTS; ++k)
+    if (k < nslots) hist_add(hist, true, kv[k] >> 20);
+  wait_vmem_all();
+  __syncthreads();
+#pragma unroll 2
+  for (int k = RSLOTS; k < nslots; ++k) hist_add(hist, true, lkey(k) >> 20);
+  __syncthreads();
+  pick(K);
+  uint32_t prefix = sel_digit << 20, pmask = 4095u << 20;
+  int remaining = K - (int)sel_below;
+  const uint32_t nbin = hist[sel_digit];     // keys sharing the first digit
+  __syncthreads();                            // everyone has read hist before it is cleared
+
+  // Passes 2 and 3 look only at keys that share the first digit.  When they
+  // fit, they are first gathered into the count array (order does not matter
+  // to a histogram), so these passes cost no more than their number; else the
+  // passes walk the row again.
+  uint32_t* cand = cand_area;
+  const bool gathered = nbin <= (uint32_t)CAND_CAP;
+  if (gathered) {
+    auto gather = [&](uint32_t key) {
+      const bool m = (key & pmask) == prefix;
+      const uint64_t b = __ballot(m);
+      uint32_t base = 0;
+      if (lane == 0 && b) base = atomicAdd(&ncand, (uint32_t)__popcll(b));
+      base = __shfl(base, 0);
+      const uint64_t below = (lane == 0) ? 0ull : (b & (~0ull >> (64 - lane)));
+      const uint32_t at = base + (uint32_t)__popcll(below);
+      if (m && at < (uint32_t)CAND_CAP) cand[at] = key;   // at < nbin <= CAND_CAP by construction
+    };
+#pragma unroll
+    for (int k = 0; k < RSLOTS; ++k)
+      if (k < nslots) gather(kv[k]);
+    for (int k = RSLOTS; k < nslots; ++k) gather(lkey(k));
+    __syncthreads();
+  }
+  const uint32_t nc = gathered ? ncand : 0u;
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 8 : 0;
+    const uint32_t dmask = pass == 2 ? 255u : 4095u;
+    for (int i = tid; i < HBINS; i += TOPK_NT) hist[i] = 0u;
+    __syncthreads();
+    if (gathered) {
+      for (uint32_t j0 = 0; j0 < nc; j0 += TOPK_NT) {
+        const uint32_t j = j0 + (uint32_t)tid;
+        const uint32_t key = j < nc ? cand[j] : 0u;
+        hist_add(hist, j < nc && (key & pmask) == prefix, (key >> shift) & dmask);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < RSLOTS; ++k)
+        if (k < nslots) hist_add(hist, (kv[k] & pmask) == prefix, (kv[k] >> shift) & dmask);
+#pragma unroll 2
+      for (int k = RSLOTS; k < nslots; ++k) {
+        const uint32_t key = lkey(k);
+        hist_add(hist, (key & pmask) == prefix, (key >> shift) & dmask);
+      }
+    }
+    __syncthreads();
+    pick(remaining);
     prefix |= sel_digit << shift;
     pmask |= dmask << shift;
     remaining -= (int)sel_below;
