@@ -410,25 +410,36 @@ __global__ __launch_bounds__(PD_NT) void pddp_project(PddpParams p) {
   const float muv = dv[D];
   const uint16_t* __restrict__ qh = p.q + head * D;
   const int32_t* __restrict__ ph = p.perm + head + off;
-  for (int base = m0; base < m1; base += RPP) {
-    const int m = base + sub;
-    const bool ok = m < m1;
-    int id = 0;
-    float part = 0.f;
-    if (ok) {
-      id = ph[m];
-      const u32x4_t x = ldg16(qh + (size_t)clamp_id(id, p.N) * D + chunk * 8);
+  // UR rows per thread and pass, their loads issued together
+  constexpr int UR = 4;
+  for (int base = m0; base < m1; base += RPP * UR) {
+    int id[UR];
+    u32x4_t x[UR];
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        part = fmaf(bf16_lo(x[wd]), vc[2 * wd], part);
-        part = fmaf(bf16_hi(x[wd]), vc[2 * wd + 1], part);
-      }
+    for (int u = 0; u < UR; ++u) {
+      const int m = base + u * RPP + sub;
+      id[u] = m < m1 ? ph[m] : 0;
     }
 #pragma unroll
-    for (int o = CH / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-    if (ok && chunk == 0) {
-      p.proj[head + off + m] = part - muv;
-      p.tmp[head + off + m] = id;
+    for (int u = 0; u < UR; ++u) {
+      const int m = base + u * RPP + sub;
+      x[u] = m < m1 ? ldg16(qh + (size_t)clamp_id(id[u], p.N) * D + chunk * 8) : zero_u32x4();
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int m = base + u * RPP + sub;
+      float part = 0.f;
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        part = fmaf(bf16_lo(x[u][wd]), vc[2 * wd], part);
+        part = fmaf(bf16_hi(x[u][wd]), vc[2 * wd + 1], part);
+      }
+#pragma unroll
+      for (int o = CH / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+      if (m < m1 && chunk == 0) {
+        p.proj[head + off + m] = part - muv;
+        p.tmp[head + off + m] = id[u];
+      }
     }
   }
 }
