@@ -87,7 +87,8 @@ def _select_case(mcs, B, H, N, D, C, K, seed, perm_kind="random"):
 
 
 @pytest.mark.parametrize("B,H,N,D,C,K", [(1, 2, 1000, 128, 128, 200), (1, 1, 700, 64, 64, 65),
-                                         (2, 1, 333, 64, 128, 1), (1, 1, 256, 128, 64, 256)])
+                                         (2, 1, 333, 64, 128, 1), (1, 1, 256, 128, 64, 256),
+                                         (1, 1, 50, 64, 64, 7), (1, 2, 100, 128, 128, 100)])
 def test_select_matches_oracle(mcs, B, H, N, D, C, K):
     _select_case(mcs, B, H, N, D, C, K, seed=N + K)
 
