@@ -4,7 +4,6 @@ and a multi-layer reuse step gives the same outputs with offloaded and with
 resident entries."""
 import math
 
-import numpy as np
 import pytest
 import torch
 
