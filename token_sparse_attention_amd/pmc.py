@@ -19,12 +19,15 @@ bench.py reports the traffic only while the kernels are unchanged.
 --util summarises one run of
 
     rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES \
+        SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS \
         GRBM_GUI_ACTIVE -d UTIL_DIR -o pmc --output-format csv -- python3 bench.py ...
 
 per kernel: the average shader clock over the dispatch (GRBM_GUI_ACTIVE, summed
 over the 8 XCDs, divided by the dispatch time), the share of SIMD cycles in
-which the MFMA unit was busy, and the share in which a plain VALU
-instruction issued while it was (co-execution).
+which the MFMA unit was busy, the share in which a plain VALU instruction
+issued while it was (co-execution), the share of SIMD cycles with a VALU
+instruction (MFMA included) executing (SQ_ACTIVE_INST_VALU counts quad-cycles
+per wave), and the VALU (MFMA excluded) and LDS instructions per MFMA.
 
 --l2 summarises one run of
 
@@ -124,6 +127,12 @@ def utilisation(util_dir: str) -> dict:
         a["mfma_busy"] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (N_SIMD * cyc)
         a["coexec"] += c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / (N_SIMD * cyc)
         a["cu_busy"] += c.get("SQ_BUSY_CU_CYCLES", 0.0) * 4 / (256 * cyc)
+        if "SQ_ACTIVE_INST_VALU" in c:
+            a["valu_active"] += c["SQ_ACTIVE_INST_VALU"] * 4 / (N_SIMD * cyc)
+        mf = c.get("SQ_INSTS_MFMA", 0.0)
+        if mf > 0:
+            a["valu_per_mfma"] += (c.get("SQ_INSTS_VALU", 0.0) - mf) / mf
+            a["lds_per_mfma"] += c.get("SQ_INSTS_LDS", 0.0) / mf
     out = {}
     for name, a in acc.items():
         n = a.pop("n")
@@ -158,7 +167,7 @@ def main(argv):
             json.dump(out, f, indent=1)
         for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["ms"]):
             print(f"{k:48s} {v['ms']:9.3f} ms  clock {v['clock_ghz']:.3f} GHz  MFMA busy {100 * v['mfma_busy']:5.1f}%"
-                  f"  co-exec {100 * v['coexec']:5.1f}%")
+                  f"  co-exec {100 * v['coexec']:5.1f}%  VALU active {100 * v.get('valu_active', 0):5.1f}%")
         return 0
     if len(argv) < 3:
         print(__doc__)
