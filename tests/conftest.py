@@ -7,6 +7,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# A planted mistake in the oracle (tests/oracle_mutants.py), applied before any
+# test module imports the oracle; used only by tests/test_oracle_mutations.py.
+if os.environ.get("MCS_ORACLE_MUTANT"):
+    from tests import oracle_mutants
+
+    oracle_mutants.apply(os.environ["MCS_ORACLE_MUTANT"])
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -1,0 +1,80 @@
+"""Planted mistakes in the oracle, for checking that its pins catch them.
+
+Each mutant replaces one exact piece of the oracle's source with a plausible
+slip (a dropped term, a wrong sign, a wrong operand or index, a wrong rule).
+tests/conftest.py applies the mutant named by the environment variable
+MCS_ORACLE_MUTANT before any test imports the oracle, by loading the mutated
+source in place of the oracle module; tests/test_oracle_mutations.py runs the
+oracle's pin tests once per mutant and requires every run to fail.  The oracle
+files themselves are never changed.
+"""
+from __future__ import annotations
+
+import importlib.util
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MCS = "oracle/mcs_oracle.py"
+DIAG = "oracle/diagnostics.py"
+
+# name -> (file, original text, mutated text)
+MUTANTS = {
+    "scores_drop_scale": (MCS, "return float(scale) * (_f64(q) @ _f64(k).T)", "return (_f64(q) @ _f64(k).T)"),
+    "lse_drop_max": (MCS, "lse[r0:r0 + ROW_BLOCK] = (m + np.log(z))[:, 0]",
+                     "lse[r0:r0 + ROW_BLOCK] = (np.log(z))[:, 0]"),
+    "dense_unnormalised": (MCS, "out[r0:r0 + ROW_BLOCK] = (e / z) @ v", "out[r0:r0 + ROW_BLOCK] = e @ v"),
+    "probabilities_sign": (MCS, "np.exp(attention_scores(q, k, scale) - _f64(lse)[:, None])",
+                           "np.exp(attention_scores(q, k, scale) + _f64(lse)[:, None])"),
+    "mass_mean_not_sum": (MCS, "probabilities(q[members], k, lse[members], scale).sum(axis=0)",
+                          "probabilities(q[members], k, lse[members], scale).mean(axis=0)"),
+    "topk_ties_to_larger_id": (MCS, "order = np.lexsort((j, -mass_row))", "order = np.lexsort((-j, -mass_row))"),
+    "topk_skips_the_largest": (MCS, "return np.sort(order[:K]).astype(np.int64)",
+                               "return np.sort(order[1:K + 1]).astype(np.int64)"),
+    "topk_not_ascending": (MCS, "return np.sort(order[:K]).astype(np.int64)", "return order[:K].astype(np.int64)"),
+    "sparse_not_renormalised": (MCS, "out[members] = (e / e.sum(axis=1, keepdims=True)) @ v[sel]",
+                                "out[members] = e @ v[sel]"),
+    "sparse_keys_as_values": (MCS, "out[members] = (e / e.sum(axis=1, keepdims=True)) @ v[sel]",
+                              "out[members] = (e / e.sum(axis=1, keepdims=True)) @ k[sel]"),
+    "residual_sign": (MCS, "return _f64(o_dense) - _f64(o_sparse)", "return _f64(o_sparse) - _f64(o_dense)"),
+    "covariance_not_centred": (MCS, "    xc = x - mu\n", "    xc = x\n"),
+    "sign_rule_flipped": (MCS, "return -vec if vec[i] < 0 else vec", "return -vec if vec[i] > 0 else vec"),
+    "power_start_smallest_diagonal": (MCS, "vec = cov[:, int(np.argmax(np.diag(cov)))].copy()",
+                                      "vec = cov[:, int(np.argmin(np.diag(cov)))].copy()"),
+    "split_rank_ceil": (MCS, "r = C * (g // 2)", "r = C * (-(-g // 2))"),
+    "split_order_descending": (MCS, "order = np.lexsort((ids, proj))", "order = np.lexsort((ids, -proj))"),
+    "variance_over_groups": (MCS, "    return total / q.shape[0]\n", "    return total / len(groups_from_perm(perm, C))\n"),
+    "perquery_keeps_one_less": (DIAG, "need = K - gt.sum(axis=1, keepdims=True)",
+                                "need = K - 1 - gt.sum(axis=1, keepdims=True)"),
+    "token_oracle_smallest_mass": (DIAG, '"token_oracle": _top_ids(mass, K),', '"token_oracle": _top_ids(-mass, K),'),
+    "kmeans_farthest_centre": (DIAG, "labels = np.argmin(d, axis=1)", "labels = np.argmax(d, axis=1)"),
+    "inflation_rounds_down": (DIAG, "(-(-sizes // tile) * tile)", "((sizes // tile) * tile)"),
+}
+
+
+def mutated_source(name: str) -> tuple[str, str]:
+    path, old, new = MUTANTS[name]
+    src = open(os.path.join(ROOT, path)).read()
+    if src.count(old) != 1:
+        raise AssertionError(f"mutant {name}: the text to replace occurs {src.count(old)} times in {path}")
+    return path, src.replace(old, new)
+
+
+def apply(name: str) -> None:
+    """Load the oracle with the named mutant in place of the original module."""
+    import oracle
+    path, src = mutated_source(name)
+    modname = "oracle.mcs_oracle" if path == MCS else "oracle.diagnostics"
+    spec = importlib.util.spec_from_loader(modname, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__package__ = "oracle"
+    mod.__file__ = os.path.join(ROOT, path)
+    sys.modules[modname] = mod
+    exec(compile(src, mod.__file__, "exec"), mod.__dict__)
+    if path == MCS:
+        for attr in getattr(mod, "__all__", []) + ["default_scale"]:
+            setattr(oracle, attr, getattr(mod, attr))
+        setattr(oracle, "mcs_oracle", mod)
+        sys.modules.pop("oracle.diagnostics", None)      # re-imported against the mutant
+    else:
+        setattr(oracle, "diagnostics", mod)

@@ -137,11 +137,13 @@ def test_pddp_bh_shape():
 
 
 def test_odd_group_count_splits_at_floor_half():
-    # N = 3C with C = 2.  The root's principal direction is along x, so the split
-    # at rank C*floor(3/2) = 2 puts {A, B} left and {C, D, E, F} right; the right
-    # node spreads along y and splits into {C, E} and {D, F}.  (A split at
-    # C*ceil(3/2) = 4 would give {A, B}, {C, D}, {E, F} instead.)
-    pts = np.array([[0.0, 0.0], [1.0, 0.0], [10.0, 0.0], [10.0, 5.0], [11.0, 0.0], [11.0, 5.0]])
+    # N = 3C with C = 2.  A and B sit at the mean height, so x and y are
+    # uncorrelated and the root's principal direction is exactly x: the split
+    # at rank C*floor(3/2) = 2 puts {A, B} left and {C, D, E, F} right, and the
+    # right node spreads along y and splits into {C, E} and {D, F}.  A split at
+    # C*ceil(3/2) = 4 would put {A, B, C, D} left (split along x into {A, B},
+    # {C, D}) and leave {E, F}.
+    pts = np.array([[0.0, 1.5], [1.0, 1.5], [10.0, 0.0], [10.0, 3.0], [10.2, 0.0], [10.2, 3.0]])
     perm = oracle.pddp(pts, 2)
     groups = [set(g.tolist()) for g in oracle.groups_from_perm(perm, 2)]
     assert groups == [{0, 1}, {2, 4}, {3, 5}]
