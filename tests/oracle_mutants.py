@@ -44,6 +44,12 @@ MUTANTS = {
     "split_rank_ceil": (MCS, "r = C * (g // 2)", "r = C * (-(-g // 2))"),
     "split_order_descending": (MCS, "order = np.lexsort((ids, proj))", "order = np.lexsort((ids, -proj))"),
     "variance_over_groups": (MCS, "    return total / q.shape[0]\n", "    return total / len(groups_from_perm(perm, C))\n"),
+    "power_one_step_short": (MCS, "for _ in range(power_iters):", "for _ in range(power_iters - 1):"),
+    "groups_drop_ragged_tail": (MCS, "return [perm[g * C:min((g + 1) * C, n)] for g in range(-(-n // C))]",
+                                "return [perm[g * C:min((g + 1) * C, n)] for g in range(n // C)]"),
+    "mean_pooling_uses_max": (DIAG, "k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].mean(axis=0)",
+                              "k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].max(axis=0)"),
+    "recall_not_averaged": (DIAG, '{"recall": rec[K][s] / Nq,', '{"recall": rec[K][s],'),
     "perquery_keeps_one_less": (DIAG, "need = K - gt.sum(axis=1, keepdims=True)",
                                 "need = K - 1 - gt.sum(axis=1, keepdims=True)"),
     "token_oracle_smallest_mass": (DIAG, '"token_oracle": _top_ids(mass, K),', '"token_oracle": _top_ids(-mass, K),'),

@@ -147,3 +147,20 @@ def test_odd_group_count_splits_at_floor_half():
     perm = oracle.pddp(pts, 2)
     groups = [set(g.tolist()) for g in oracle.groups_from_perm(perm, 2)]
     assert groups == [{0, 1}, {2, 4}, {3, 5}]
+
+
+@pytest.mark.parametrize("steps", [1, 7, 32])
+def test_power_iteration_closed_form_after_t_steps(steps):
+    # four points +-sqrt(2) u1, +-sqrt(1.8) u2 with u1 = (1, 1)/sqrt2, u2 =
+    # (1, -1)/sqrt2: mean 0, covariance eigenvalues 1 (u1) and 0.9 (u2), i.e.
+    # [[0.95, 0.05], [0.05, 0.95]].  The start column is column 0 (equal
+    # diagonals: the first), (0.95, 0.05) = (u1 + 0.9 u2)/sqrt2, so after t
+    # steps the direction is proportional to u1 + 0.9^(t+1) u2.
+    u1 = np.array([1.0, 1.0]) / np.sqrt(2)
+    u2 = np.array([1.0, -1.0]) / np.sqrt(2)
+    pts = np.stack([np.sqrt(2) * u1, -np.sqrt(2) * u1, np.sqrt(1.8) * u2, -np.sqrt(1.8) * u2])
+    mu, vec = oracle.principal_direction(pts, mode="power", power_iters=steps)
+    want = u1 + 0.9 ** (steps + 1) * u2
+    want /= np.linalg.norm(want)
+    np.testing.assert_allclose(mu, 0.0, atol=1e-15)
+    np.testing.assert_allclose(vec, want, rtol=0, atol=1e-12)
