@@ -50,6 +50,17 @@ MUTANTS = {
     "mean_pooling_uses_max": (DIAG, "k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].mean(axis=0)",
                               "k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].max(axis=0)"),
     "recall_not_averaged": (DIAG, '{"recall": rec[K][s] / Nq,', '{"recall": rec[K][s],'),
+    "reuse_subtracts_residual": (MCS, "out = out + _f64(residual)", "out = out - _f64(residual)"),
+    "lse_log2": (MCS, "lse[r0:r0 + ROW_BLOCK] = (m + np.log(z))[:, 0]",
+                 "lse[r0:r0 + ROW_BLOCK] = (m + np.log2(z))[:, 0]"),
+    "pddp_default_eigh": (MCS, 'def pddp(q, C: int, mode: str = "power"', 'def pddp(q, C: int, mode: str = "eigh"'),
+    "retained_mass_first_ids": (MCS, "mass[g, np.asarray(idx[g])].sum()", "mass[g, :len(idx[g])].sum()"),
+    "block_keys_off_by_one": (DIAG, "keys = (blocks[:, None] * KV_BLOCK + np.arange(KV_BLOCK)[None, :]).ravel()",
+                              "keys = (blocks[:, None] * KV_BLOCK + 1 + np.arange(KV_BLOCK)[None, :]).ravel()"),
+    "kmeans_centre_is_sum": (DIAG, "c[nz] = sums[nz] / counts[nz][:, None]", "c[nz] = sums[nz]"),
+    "inflation_over_clusters": (DIAG, "return float((-(-sizes // tile) * tile).sum() / sizes.sum())",
+                                "return float((-(-sizes // tile) * tile).sum() / sizes.size)"),
+    "topk_smallest_mass": (MCS, "order = np.lexsort((j, -mass_row))", "order = np.lexsort((j, mass_row))"),
     "perquery_keeps_one_less": (DIAG, "need = K - gt.sum(axis=1, keepdims=True)",
                                 "need = K - 1 - gt.sum(axis=1, keepdims=True)"),
     "token_oracle_smallest_mass": (DIAG, '"token_oracle": _top_ids(mass, K),', '"token_oracle": _top_ids(-mass, K),'),

@@ -98,6 +98,12 @@ def test_default_direction_is_power_iteration():
     for mode in ("eigh", "power"):
         perm = oracle.pddp(q, 16, mode=mode)
         assert sorted(perm.tolist()) == list(range(300))
+    # two leading variances 3% apart: 32 steps leave the direction short of the
+    # eigenvector, so the default must group differently from exact eigenvectors
+    q = _rand((256, 3), 0) * np.array([1.0, 0.97, 0.3])
+    sets = lambda perm: {frozenset(g.tolist()) for g in oracle.groups_from_perm(perm, 32)}
+    assert sets(oracle.pddp(q, 32, mode="eigh")) != sets(oracle.pddp(q, 32, mode="power"))
+    assert np.array_equal(oracle.pddp(q, 32), oracle.pddp(q, 32, mode="power", power_iters=32))
 
 
 def test_power_mode_with_many_steps_matches_eigh_grouping():
