@@ -28,7 +28,7 @@ Conventions (all arrays are numpy, all arithmetic is float64):
     0..N-1; group g is perm[g*C : min((g+1)*C, N)], G = ceil(N / C).
   * ``idx`` holds, per group, the K selected KV token ids (ascending).
 
-Readings of points the pages leave open (each listed in the design doc as well):
+Readings of points the pages leave open:
   R1 softmax scale tau = 1/sqrt(D) is passed in by the caller;
   R2 no mask: every query sees all N keys (bidirectional DiT attention);
   R3 top-K ties: larger mass first, equal mass -> smaller KV id; output ascending;
