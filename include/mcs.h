@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MCS_VERSION 100
+#define MCS_VERSION 101
 
 #if defined(__GNUC__)
 #define MCS_API __attribute__((visibility("default")))
@@ -152,10 +152,24 @@ MCS_API mcs_status mcs_residual_update(const uint16_t* o_dense, const uint16_t* 
  * int32 [B,H,N].  Out: kv_idx int32 [B,H,G,K].  ws: device workspace of at
  * least mcs_select_workspace(d, C, K) bytes (the per-group mass rows of a
  * chunk of heads; a larger workspace processes more heads per launch).
+ * Aggregation and top-K run in one kernel, as on the ai.info page: each
+ * workgroup writes its group's mass row and selects from it before it ends.
+ * Where that kernel's compaction counts do not fit in LDS (N > 262144 for
+ * D = 128, N > 131072 for D = 64) a separate top-K kernel follows instead;
+ * the ids are the same either way.
  */
 MCS_API mcs_status mcs_select(const uint16_t* q, const uint16_t* k, const float* lse,
                       const int32_t* perm, int32_t* kv_idx, mcs_dims d, int32_t C,
                       int32_t K, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mcs_select always as two kernels: the mass rows of a chunk of heads, then
+ * the top-K of every row.  Same arguments, workspace, checks and results.
+ */
+MCS_API mcs_status mcs_select_two_pass(const uint16_t* q, const uint16_t* k, const float* lse,
+                               const int32_t* perm, int32_t* kv_idx, mcs_dims d, int32_t C,
+                               int32_t K, float scale, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Minimum workspace of mcs_select (one head's mass rows: G * N * 4 bytes). */
 MCS_API size_t mcs_select_workspace(mcs_dims d, int32_t C, int32_t K);

@@ -44,6 +44,7 @@ def lib():
     lib.mcs_sparse_attn_f32out.argtypes = [P, P, P, P, P, P, P, Dims, I32, I32, F, P]
     lib.mcs_residual_update.argtypes = [P, P, P, I64, P]
     lib.mcs_select.argtypes = [P, P, P, P, P, Dims, I32, I32, F, P, SZ, P]
+    lib.mcs_select_two_pass.argtypes = [P, P, P, P, P, Dims, I32, I32, F, P, SZ, P]
     lib.mcs_topk.argtypes = [P, P, I64, I32, I32, P]
     lib.mcs_group.argtypes = [P, P, Dims, I32, I32, P, SZ, P]
     lib.mcs_group_workspace.argtypes = [Dims, I32]
@@ -59,7 +60,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -127,6 +128,13 @@ def test_select_group_topk_residual_validation(lib):
     assert lib.mcs_select(A, B_, C_, D_, E_, d, 128, 100, 0.1, None, need, None) == c["MCS_E_WORKSPACE"]
     assert lib.mcs_select(A, B_, C_, D_, E_, d, 128, 100, 0.1, 0x80000, need - 1, None) == c["MCS_E_WORKSPACE"]
     assert lib.mcs_select(A, B_, None, D_, E_, d, 128, 100, 0.1, 0x80000, need, None) == c["MCS_E_NULL"]
+    for fn in (lib.mcs_select, lib.mcs_select_two_pass):
+        assert fn(A, B_, C_, D_, E_, d, 128, 100, 0.1, 0x80000, need - 1, None) == c["MCS_E_WORKSPACE"]
+        assert fn(A, B_, C_, None, E_, d, 128, 100, 0.1, 0x80000, need, None) == c["MCS_E_NULL"]
+        assert fn(A, B_, C_, D_, E_, d, 100, 100, 0.1, 0x80000, need, None) == c["MCS_E_GROUP_SIZE"]
+        assert fn(A, B_, C_, D_, E_, Dims(1, 2, 1000, 96), 128, 100, 0.1, 0x80000, need, None) == c["MCS_E_HEAD_DIM"]
+        assert fn(A, B_, C_, D_, E_, d, 128, 1001, 0.1, 0x80000, need, None) == c["MCS_E_BUDGET"]
+        assert fn(A, B_, C_, D_, E_, d, 128, 100, 0.1, 0x80004, need, None) == c["MCS_E_ALIGN"]
     gws = lib.mcs_group_workspace(d, 128)
     assert gws >= 2 * 2 * 1000 * 4
     assert lib.mcs_group(A, B_, d, 128, 0, 0x80000, gws - 1, None) == c["MCS_E_WORKSPACE"]

@@ -4,7 +4,10 @@ mcs_topk is compared decision-for-decision with the oracle's top-K applied to
 the same float32 score rows (both sides decide in float32), including rows
 with many ties.  mcs_select is compared with the oracle's fp64 selection on
 the same groups: the ids may differ only among masses within 1e-6 of the K-th
-largest, and the retained mass must agree to 1e-4 relative.
+largest, and the retained mass must agree to 1e-4 relative.  mcs_select (mass
+and top-K in one kernel where the row's counts fit in LDS) and
+mcs_select_two_pass (mass kernel, then top-K kernel) compute the same fp32
+masses and apply the same rule, so their ids must be identical.
 """
 import math
 
@@ -77,7 +80,9 @@ def _select_case(mcs, B, H, N, D, C, K, seed, perm_kind="random"):
         perm = oracle.pddp_bh(qf, C).astype(np.int32)
     _, lse = oracle.dense_attention_bh(qf, kf, qf, scale)
     ref_idx, ref_mass = oracle.select_bh(qf, kf, lse, perm, C, K, scale)
-    got = mcs.select(to_dev_bf16(q), to_dev_bf16(k), to_dev(lse.astype(np.float32)), to_dev(perm), C, K, scale)
+    args = (to_dev_bf16(q), to_dev_bf16(k), to_dev(lse.astype(np.float32)), to_dev(perm), C, K, scale)
+    got = mcs.select(*args)
+    assert torch.equal(got, mcs.select_two_pass(*args))
     got = got.cpu().numpy()
     G = accounting.num_groups(N, C)
     assert got.shape == (B, H, G, K)
@@ -128,3 +133,28 @@ def test_select_with_gpu_lse(mcs):
     ref_idx, ref_mass = oracle.select_bh(qf, kf, ref_lse, perm, C, K, scale)
     for h in range(H):
         assert_index_sets_match(got[0, h], ref_idx[0, h], ref_mass[0, h], K)
+
+
+@pytest.mark.parametrize("N,D,C,K,dup", [(4097, 128, 128, 800, False), (3000, 64, 64, 1500, True),
+                                         (3001, 128, 64, 2999, True), (75600, 128, 128, 15104, False),
+                                         (131072, 64, 128, 26215, False), (131073, 64, 128, 100, False),
+                                         (65536, 128, 64, 65536, False)])
+def test_fused_select_equals_two_pass(mcs, N, D, C, K, dup):
+    """One head per case, LSE from the GPU's own dense pass: a large-workload
+    head, the largest row the fused kernel holds for D = 64 (and one past it,
+    where mcs_select takes the two-kernel route), K = N, and duplicated keys
+    (equal masses in pairs, so the tie rule decides at the K-th key)."""
+    q = synth.gaussian((1, 1, N, D), 60 + N, 1.5)
+    k = synth.gaussian((1, 1, N, D), 61 + N, 1.5)
+    if dup:
+        k[:, :, 1::2] = k[:, :, 0:N - 1:2]
+    scale = 1 / math.sqrt(D)
+    dq, dk = to_dev_bf16(q), to_dev_bf16(k)
+    _, lse = mcs.dense_attn(dq, dk, dk, scale, want_lse=True)
+    perm = to_dev(synth.random_perm(1, 1, N, seed=N))
+    print(f"[fused select] N={N} D={D} C={C} K={K} dup={dup}", flush=True)
+    a = mcs.select(dq, dk, lse, perm, C, K, scale)
+    b = mcs.select_two_pass(dq, dk, lse, perm, C, K, scale)
+    assert torch.equal(a, b)
+    ids = a[0, 0]
+    assert bool((ids[:, 1:] > ids[:, :-1]).all()) and int(ids.min()) >= 0 and int(ids.max()) < N

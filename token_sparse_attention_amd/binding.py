@@ -44,6 +44,7 @@ _SIGS = {
     "mcs_sparse_attn_f32out": ([_P, _P, _P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P], _I32),
     "mcs_residual_update": ([_P, _P, _P, _I64, _P], _I32),
     "mcs_select": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
+    "mcs_select_two_pass": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
     "mcs_select_workspace": ([Dims, _I32, _I32], _SZ),
     "mcs_select_workspace_all_heads": ([Dims, _I32, _I32], _SZ),
     "mcs_topk": ([_P, _P, _I64, _I32, _I32, _P], _I32),
@@ -200,6 +201,15 @@ def select_workspace_bytes(q_shape, C, K, all_heads=True) -> int:
 
 def select(q, k, lse, perm, C, K, scale=None, out=None, workspace=None, max_workspace_bytes=2 << 30):
     """mcs_select: exact per-group top-K KV ids from recovered probabilities."""
+    return _select(_lib.mcs_select, q, k, lse, perm, C, K, scale, out, workspace, max_workspace_bytes)
+
+
+def select_two_pass(q, k, lse, perm, C, K, scale=None, out=None, workspace=None, max_workspace_bytes=2 << 30):
+    """mcs_select_two_pass: the same selection as a mass kernel followed by a top-K kernel."""
+    return _select(_lib.mcs_select_two_pass, q, k, lse, perm, C, K, scale, out, workspace, max_workspace_bytes)
+
+
+def _select(fn, q, k, lse, perm, C, K, scale, out, workspace, max_workspace_bytes):
     _qkv(q, k)
     B, H, N, D = q.shape
     _need(lse, "lse", torch.float32, 3)
@@ -211,8 +221,8 @@ def select(q, k, lse, perm, C, K, scale=None, out=None, workspace=None, max_work
         per_head = select_workspace_bytes(q.shape, C, K, all_heads=False)
         nbytes = min(select_workspace_bytes(q.shape, C, K), max(per_head, max_workspace_bytes // per_head * per_head))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _check(_lib.mcs_select(_ptr(q), _ptr(k), _ptr(lse), _ptr(perm), _ptr(out), dims_of(q), C, K, scale,
-                           _ptr(workspace), workspace.numel(), _stream(q)))
+    _check(fn(_ptr(q), _ptr(k), _ptr(lse), _ptr(perm), _ptr(out), dims_of(q), C, K, scale,
+              _ptr(workspace), workspace.numel(), _stream(q)))
     return out
 
 

@@ -170,10 +170,10 @@ size_t mcs_select_workspace_all_heads(mcs_dims d, int32_t C, int32_t K) {
   return select_ws_per_head(d, C) * (size_t)d.B * (size_t)d.H;
 }
 
-mcs_status mcs_select(const uint16_t* q, const uint16_t* k, const float* lse, const int32_t* perm,
-                      int32_t* kv_idx, mcs_dims d, int32_t C, int32_t K, float scale, void* ws,
-                      size_t ws_bytes, void* stream) {
-  const char* fn = "mcs_select";
+static mcs_status select_impl(const char* fn, bool fused, const uint16_t* q, const uint16_t* k,
+                              const float* lse, const int32_t* perm, int32_t* kv_idx, mcs_dims d,
+                              int32_t C, int32_t K, float scale, void* ws, size_t ws_bytes,
+                              void* stream) {
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(lse);
@@ -197,12 +197,33 @@ mcs_status mcs_select(const uint16_t* q, const uint16_t* k, const float* lse, co
   float* mass = static_cast<float*>(ws);
   for (int bh0 = 0; bh0 < BH; bh0 += chunk) {
     const int nh = BH - bh0 < chunk ? BH - bh0 : chunk;
-    hipError_t e = mcs::run_group_mass(q, k, lse, perm, mass, bh0, nh, d.N, d.D, C, scale, s);
-    if (e == hipSuccess)
-      e = mcs::run_topk(mass, kv_idx + (size_t)bh0 * G * K, (int64_t)nh * G, d.N, K, s);
+    int32_t* idx = kv_idx + (size_t)bh0 * G * K;
+    hipError_t e;
+    if (fused) {
+      e = mcs::run_select_fused(q, k, lse, perm, mass, idx, bh0, nh, d.N, d.D, C, K, scale, s);
+    } else {
+      e = mcs::run_group_mass(q, k, lse, perm, mass, bh0, nh, d.N, d.D, C, scale, s);
+      if (e == hipSuccess) e = mcs::run_topk(mass, idx, (int64_t)nh * G, d.N, K, s);
+    }
     if (e != hipSuccess) return launched(fn, e);
   }
   return ok();
+}
+
+mcs_status mcs_select(const uint16_t* q, const uint16_t* k, const float* lse, const int32_t* perm,
+                      int32_t* kv_idx, mcs_dims d, int32_t C, int32_t K, float scale, void* ws,
+                      size_t ws_bytes, void* stream) {
+  const bool fused = d.N >= 1 && (d.D == 64 || d.D == 128) && (C == 64 || C == 128) &&
+                     mcs::select_fused_fits(d.N, d.D, C);
+  return select_impl("mcs_select", fused, q, k, lse, perm, kv_idx, d, C, K, scale, ws, ws_bytes,
+                     stream);
+}
+
+mcs_status mcs_select_two_pass(const uint16_t* q, const uint16_t* k, const float* lse,
+                               const int32_t* perm, int32_t* kv_idx, mcs_dims d, int32_t C,
+                               int32_t K, float scale, void* ws, size_t ws_bytes, void* stream) {
+  return select_impl("mcs_select_two_pass", false, q, k, lse, perm, kv_idx, d, C, K, scale, ws,
+                     ws_bytes, stream);
 }
 
 mcs_status mcs_topk(const float* scores, int32_t* idx, int64_t rows, int32_t n, int32_t K,

@@ -118,6 +118,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// head_rsrc from a base and size made wave-uniform explicitly, for kernels in
+// which the compiler would otherwise keep the descriptor in vector registers
+// (the DMA instructions need it in scalar ones).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return head_rsrc(reinterpret_cast<const void*>((uintptr_t)(((uint64_t)hi << 32) | lo)),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
+
 // One 16-byte buffer load per lane written straight to LDS: the wave writes
 // 1 KiB at lds (wave-uniform) + 16 * lane.
 //

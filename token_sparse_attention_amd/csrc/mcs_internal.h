@@ -22,6 +22,13 @@ hipError_t run_group_mass(const uint16_t* q, const uint16_t* k, const float* lse
                           const int32_t* perm, float* mass, int bh0, int nh, int N, int D,
                           int C, float scale, hipStream_t s);
 
+// Group mass rows as above, each followed in the same workgroup by its top-K
+// (idx[(h - bh0) * G + g][0, K)); only where select_fused_fits(N, D, C).
+bool select_fused_fits(int N, int D, int C);
+hipError_t run_select_fused(const uint16_t* q, const uint16_t* k, const float* lse,
+                            const int32_t* perm, float* mass, int32_t* idx, int bh0, int nh,
+                            int N, int D, int C, int K, float scale, hipStream_t s);
+
 // Top-K of non-negative rows (ties to the smaller id, ids ascending).
 hipError_t run_topk(const float* scores, int32_t* idx, int64_t rows, int n, int K,
                     hipStream_t s);

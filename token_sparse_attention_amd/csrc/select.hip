@@ -13,7 +13,12 @@
 // key per lane column, so each lane sums exp2(s*scale*log2e - lse_i*log2e)
 // over its 16 query rows, adds its partner lane's half, and the C/32 waves
 // combine through LDS in a fixed order.  One fp32 mass row of N values per
-// group goes to the workspace.
+// group goes to the workspace.  The fused form (aggregation and top-K in one
+// kernel, as the ai.info page describes the second pass) also histograms the
+// first digit of each finished mass during the sweep, then selects the K ids
+// from the row it has just written, in the same workgroup: two more digit
+// passes and the compaction read the row back (from cache while it is fresh),
+// and the other workgroups' VALU-bound sweeps on the CU hide those reads.
 //
 // topk_reg_kernel: one 1024-thread workgroup per mass row of up to 81920
 // values, held on chip (registers and LDS): radix select of the K-th largest
@@ -39,11 +44,19 @@ struct MassParams {
   const float* lse;
   const int32_t* perm;
   float* mass;
-  int32_t N, C, G, bh0, nh;
+  int32_t* idx;    // fused top-K: the chunk's [nh * G, K] ids
+  int32_t N, C, G, bh0, nh, K;
   float sl2;
 };
 
-template <int D, int NW>
+// Order key of a mass (a non-negative float): larger mass -> smaller key;
+// -0.0 (and any negative value, which cannot occur) ranks as 0.  The full
+// 32-bit key always has its top bit set, so 31 bits order the row.
+__device__ __forceinline__ uint32_t mass_key31(uint32_t u) {
+  return ~((u & 0x80000000u) ? 0u : u) & 0x7fffffffu;
+}
+
+template <int D, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int ROWB = D * 2;               // bytes per K row
@@ -57,16 +70,23 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
 
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][MKT * D];
   __shared__ float red[2][NW][MKT];
+  // fused top-K: histogram of the first 9-bit digit of the keys, filled as
+  // the masses are completed
+  constexpr int H1 = 512;
+  __shared__ uint32_t h1[FUSED ? H1 : 1];
   char* const lbase = reinterpret_cast<char*>(&lds_k[0][0]);
 
   const int tid = threadIdx.x;
+  if (FUSED)
+    for (int i = tid; i < H1; i += NW * 64) h1[i] = 0u;
   const int lane = tid & 63, lq = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lb = xcd_remap(blockIdx.x, p.nh * p.G);
   const int hl = lb / p.G, g = lb - hl * p.G;
   const size_t head = (size_t)(p.bh0 + hl) * p.N;
   const uint16_t* __restrict__ qh = p.q + head * D;
-  const __amdgpu_buffer_rsrc_t rk = head_rsrc(p.k + head * D, (uint32_t)p.N * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = FUSED ? head_rsrc_uniform(p.k + head * D, (uint32_t)p.N * ROWB)
+                                          : head_rsrc(p.k + head * D, (uint32_t)p.N * ROWB);
 
   // A fragments: row lq of the wave's 32-query block
   const int qpos = g * p.C + w * 32 + lq;
@@ -133,6 +153,7 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) s += red[b][ww][kk];
       mrow[key] = s;
+      if (FUSED) atomicAdd(&h1[mass_key31(__float_as_uint(s)) >> 22], 1u);
     }
   };
 
@@ -172,6 +193,189 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   if (t < ntiles) step(std::integral_constant<int, 0>{}, t);
   __syncthreads();
   store_tile(ntiles - 1);
+  if (!FUSED) return;
+
+  // ---- fused top-K over the group's own mass row, just written ----
+  // Radix select of the K-th smallest 31-bit key in digits of 9 (histogram
+  // built during the sweep), 11 and 11 bits, then the order-preserving
+  // compaction (ties to the smaller id); the row is read back four times
+  // (two digit passes, counting, placing), in rounds of NT * V positions with
+  // V consecutive keys per thread (one 16-byte load when N % 4 == 0, so rows
+  // are 16-byte aligned; else V = 1).  Scratch reuses the K tiles' LDS: an
+  // 11-bit histogram, then the compaction's per-(round, wave) counts.
+  constexpr int NT = NW * 64;
+  constexpr int H2 = 2048;
+  static_assert(sizeof(lds_k) >= H2 * 4, "scratch for the 11-bit histogram");
+  __shared__ uint32_t wtot[NW];
+  __shared__ uint32_t sel_digit, sel_below;
+  uint32_t* const sh = reinterpret_cast<uint32_t*>(lbase);
+  const uint32_t* __restrict__ xr = reinterpret_cast<const uint32_t*>(mrow);
+  int32_t* __restrict__ out = p.idx + ((size_t)hl * p.G + g) * p.K;
+  const int N = p.N;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  __syncthreads();                           // row and first histogram complete
+
+  // the bin of hist[0, NB) that holds the remaining-th smallest key: thread t
+  // owns bins NB/NT * t ...; sets sel_digit and sel_below (keys in smaller bins)
+  auto pick = [&](auto nb_c, const uint32_t* hist, uint32_t remaining) {
+    constexpr int NB = decltype(nb_c)::value;
+    constexpr int BPT = NB / NT;
+    static_assert(NB % NT == 0, "bins split evenly over the threads");
+    uint32_t c[BPT];
+    uint32_t local = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      c[q] = hist[BPT * tid + q];
+      local += c[q];
+    }
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wtot[w] = incl;
+    __syncthreads();
+    uint32_t wbase = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww)
+      if (ww < w) wbase += wtot[ww];
+    const uint32_t excl = wbase + incl - local;
+    if (excl < remaining && remaining <= excl + local) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        if (acc + c[q] >= remaining) {
+          sel_digit = BPT * tid + q;
+          sel_below = acc;
+          break;
+        }
+        acc += c[q];
+      }
+    }
+    __syncthreads();
+  };
+
+  auto select_row = [&](auto v_c) {
+    constexpr int V = decltype(v_c)::value;
+    constexpr int RB = 8;                    // rounds per batch of loads in flight
+    const int rounds = (N + NT * V - 1) / (NT * V);   // the host keeps 2 * rounds * NW <= sh's size
+    // f(round, first position, keys) for every round; positions past N hold
+    // the key of a zero mass and are excluded by the callers
+    auto walk = [&](auto f) {
+      for (int r0 = 0; r0 < rounds; r0 += RB) {
+        uint32_t u[RB][V];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          const int i = (r0 + j) * NT * V + V * tid;
+          const bool ok = r0 + j < rounds && i < N;
+          if (V == 4) {
+            const u32x4_t x = ok ? *reinterpret_cast<const u32x4_t*>(xr + i) : zero_u32x4();
+#pragma unroll
+            for (int e = 0; e < V; ++e) u[j][e] = x[e];
+          } else {
+            u[j][0] = ok ? xr[i] : 0u;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+          if (r0 + j < rounds) f(r0 + j, (r0 + j) * NT * V + V * tid, u[j]);
+      }
+    };
+
+    pick(std::integral_constant<int, H1>{}, h1, (uint32_t)p.K);
+    uint32_t prefix = sel_digit << 22, pmask = 511u << 22;
+    uint32_t remaining = (uint32_t)p.K - sel_below;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 11 : 0;
+      for (int i = tid; i < H2; i += NT) sh[i] = 0u;
+      __syncthreads();
+      walk([&](int, int i0, const uint32_t (&u)[V]) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const uint32_t key = mass_key31(u[e]);
+          if (i0 + e < N && (key & pmask) == prefix) atomicAdd(&sh[(key >> shift) & 2047u], 1u);
+        }
+      });
+      __syncthreads();
+      pick(std::integral_constant<int, H2>{}, sh, remaining);
+      prefix |= sel_digit << shift;
+      pmask |= 2047u << shift;
+      remaining -= sel_below;
+    }
+    const uint32_t T = prefix;
+    const uint32_t need = remaining;
+
+    // compaction, step 1: per round and wave, the keys below and equal to T
+    uint32_t* const cnt_lt = sh;
+    uint32_t* const cnt_eq = sh + rounds * NW;
+    walk([&](int r, int i0, const uint32_t (&u)[V]) {
+      uint32_t nlt = 0, neq = 0;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const uint32_t key = mass_key31(u[e]);
+        const bool valid = i0 + e < N;
+        nlt += (uint32_t)__popcll(__ballot(valid && key < T));
+        neq += (uint32_t)__popcll(__ballot(valid && key == T));
+      }
+      if (lane == 0) {
+        cnt_lt[r * NW + w] = nlt;
+        cnt_eq[r * NW + w] = neq;
+      }
+    });
+    __syncthreads();
+    // step 2: exclusive scans of both count arrays in position order (wave 0
+    // scans the lt counts, wave 1 the eq counts; each lane owns a contiguous run)
+    if (w < 2) {
+      uint32_t* c = w == 0 ? cnt_lt : cnt_eq;
+      const int total = rounds * NW;
+      const int per = (total + 63) / 64;
+      const int b0 = lane * per, b1 = min(total, b0 + per);
+      uint32_t local = 0;
+      for (int j = b0; j < b1; ++j) local += c[j];
+      uint32_t incl = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      uint32_t run = incl - local;
+      for (int j = b0; j < b1; ++j) {
+        const uint32_t v = c[j];
+        c[j] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    // step 3: place every chosen id: rank = #(keys < T before it) +
+    // min(#(keys == T before it), need); a wave's positions in a round are
+    // contiguous, lane-major, V per lane
+    walk([&](int r, int i0, const uint32_t (&u)[V]) {
+      bool lt[V], eq[V];
+      uint32_t lt_before = cnt_lt[r * NW + w], eq_before = cnt_eq[r * NW + w];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const uint32_t key = mass_key31(u[e]);
+        const bool valid = i0 + e < N;
+        lt[e] = valid && key < T;
+        eq[e] = valid && key == T;
+        lt_before += (uint32_t)__popcll(__ballot(lt[e]) & lt_mask);
+        eq_before += (uint32_t)__popcll(__ballot(eq[e]) & lt_mask);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (lt[e] || (eq[e] && eq_before < need)) {
+          const uint32_t rank = lt_before + (eq_before < need ? eq_before : need);
+          if (rank < (uint32_t)p.K) out[rank] = i0 + e;   // rank < K by construction; kept as a bound
+        }
+        lt_before += lt[e];
+        eq_before += eq[e];
+      }
+    });
+  };
+  if ((N & 3) == 0) select_row(std::integral_constant<int, 4>{});
+  else select_row(std::integral_constant<int, 1>{});
 }
 
 hipError_t run_group_mass(const uint16_t* q, const uint16_t* k, const float* lse,
@@ -181,13 +385,41 @@ hipError_t run_group_mass(const uint16_t* q, const uint16_t* k, const float* lse
   p.q = q; p.k = k; p.lse = lse; p.perm = perm; p.mass = mass;
   p.N = N; p.C = C; p.G = (N + C - 1) / C; p.bh0 = bh0; p.nh = nh;
   p.sl2 = scale * kLog2e;
+  p.idx = nullptr; p.K = 0;
   const dim3 grid(nh * p.G);
   if (D == 128) {
-    if (C == 128) hipLaunchKernelGGL((group_mass_kernel<128, 4>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((group_mass_kernel<128, 2>), grid, dim3(128), 0, s, p);
+    if (C == 128) hipLaunchKernelGGL((group_mass_kernel<128, 4, false>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((group_mass_kernel<128, 2, false>), grid, dim3(128), 0, s, p);
   } else {
-    if (C == 128) hipLaunchKernelGGL((group_mass_kernel<64, 4>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((group_mass_kernel<64, 2>), grid, dim3(128), 0, s, p);
+    if (C == 128) hipLaunchKernelGGL((group_mass_kernel<64, 4, false>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((group_mass_kernel<64, 2, false>), grid, dim3(128), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+// The fused kernel keeps its compaction counts (2 per round of C/32 * 64
+// positions and wave) in the LDS of the K tiles: 64 * D * 2 * 2 bytes.
+bool select_fused_fits(int N, int D, int C) {
+  const int64_t nt = (C / 32) * 64;
+  const int64_t rounds = ((int64_t)N + nt - 1) / nt;
+  return 2 * rounds * (C / 32) * 4 <= (int64_t)MKT * D * 2 * 2;
+}
+
+hipError_t run_select_fused(const uint16_t* q, const uint16_t* k, const float* lse,
+                            const int32_t* perm, float* mass, int32_t* idx, int bh0, int nh,
+                            int N, int D, int C, int K, float scale, hipStream_t s) {
+  if (!select_fused_fits(N, D, C)) return hipErrorInvalidValue;
+  MassParams p;
+  p.q = q; p.k = k; p.lse = lse; p.perm = perm; p.mass = mass; p.idx = idx;
+  p.N = N; p.C = C; p.G = (N + C - 1) / C; p.bh0 = bh0; p.nh = nh; p.K = K;
+  p.sl2 = scale * kLog2e;
+  const dim3 grid(nh * p.G);
+  if (D == 128) {
+    if (C == 128) hipLaunchKernelGGL((group_mass_kernel<128, 4, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((group_mass_kernel<128, 2, true>), grid, dim3(128), 0, s, p);
+  } else {
+    if (C == 128) hipLaunchKernelGGL((group_mass_kernel<64, 4, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((group_mass_kernel<64, 2, true>), grid, dim3(128), 0, s, p);
   }
   return hipGetLastError();
 }
