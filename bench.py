@@ -396,8 +396,9 @@ ALL_CONFIGS = [("tiny", 0.25), ("small", 0.20), ("large", 0.20), ("long", 0.25),
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
-              "head with no exchange, see the design notes", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): every stage of the path is "
+              "independent per (batch, head), so several GPUs would each run their own heads with no "
+              "exchange, and no multi-GPU figure is measured here", file=sys.stderr)
         sys.exit(2)
     import torch
 
