@@ -29,7 +29,7 @@ alignment inflation factor of k-means for blocks and for tokens; wispaper.ai
 "Token-level selection needs tile-aligned query groups"; the agihunt.info
 method paragraphs).  ``kmeans`` and ``alignment_inflation`` measure that.
 
-Readings of what the pages leave open (listed in the design notes as well):
+Readings of what the pages leave open:
   D1 KV blocks are 64 consecutive keys (the kernels' key tile); the last one
      may be short;
   D2 a query block is one query group: C consecutive queries ("contiguous"),
