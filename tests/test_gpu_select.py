@@ -138,12 +138,14 @@ def test_select_with_gpu_lse(mcs):
 @pytest.mark.parametrize("N,D,C,K,dup", [(4097, 128, 128, 800, False), (3000, 64, 64, 1500, True),
                                          (3001, 128, 64, 2999, True), (75600, 128, 128, 15104, False),
                                          (131072, 64, 128, 26215, False), (131073, 64, 128, 100, False),
-                                         (65536, 128, 64, 65536, False)])
+                                         (131071, 64, 128, 5000, False), (65536, 128, 64, 65536, False)])
 def test_fused_select_equals_two_pass(mcs, N, D, C, K, dup):
     """One head per case, LSE from the GPU's own dense pass: a large-workload
-    head, the largest row the fused kernel holds for D = 64 (and one past it,
-    where mcs_select takes the two-kernel route), K = N, and duplicated keys
-    (equal masses in pairs, so the tie rule decides at the K-th key)."""
+    head, the largest rows the fused kernel holds for D = 64 (16-byte and
+    4-byte reads; the latter leaves no LDS for the gathered third-digit keys,
+    so the counting read runs) and one past it (mcs_select takes the
+    two-kernel route), K = N, and duplicated keys (equal masses in pairs, so
+    the tie rule decides at the K-th key)."""
     q = synth.gaussian((1, 1, N, D), 60 + N, 1.5)
     k = synth.gaussian((1, 1, N, D), 61 + N, 1.5)
     if dup:
@@ -158,3 +160,21 @@ def test_fused_select_equals_two_pass(mcs, N, D, C, K, dup):
     assert torch.equal(a, b)
     ids = a[0, 0]
     assert bool((ids[:, 1:] > ids[:, :-1]).all()) and int(ids.min()) >= 0 and int(ids.max()) < N
+
+
+@pytest.mark.parametrize("N,D,C,K", [(5000, 128, 128, 1234), (3001, 64, 64, 3000)])
+def test_fused_select_all_masses_equal(mcs, N, D, C, K):
+    """Identical keys: every key of a group has the same mass, so the K ids are
+    the first K.  Every key shares the threshold's leading bits, more than the
+    fused kernel gathers, so its counting read runs."""
+    q = synth.gaussian((1, 1, N, D), 70, 1.5)
+    k = np.repeat(synth.gaussian((1, 1, 1, D), 71, 1.5), N, axis=2)
+    scale = 1 / math.sqrt(D)
+    dq, dk = to_dev_bf16(q), to_dev_bf16(k)
+    _, lse = mcs.dense_attn(dq, dk, dk, scale, want_lse=True)
+    perm = to_dev(synth.random_perm(1, 1, N, seed=N))
+    print(f"[fused select, equal masses] N={N} D={D} C={C} K={K}", flush=True)
+    a = mcs.select(dq, dk, lse, perm, C, K, scale)
+    assert torch.equal(a, mcs.select_two_pass(dq, dk, lse, perm, C, K, scale))
+    G = accounting.num_groups(N, C)
+    np.testing.assert_array_equal(a[0, 0].cpu().numpy(), np.broadcast_to(np.arange(K), (G, K)))

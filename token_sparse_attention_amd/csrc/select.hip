@@ -198,16 +198,18 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   // ---- fused top-K over the group's own mass row, just written ----
   // Radix select of the K-th smallest 31-bit key in digits of 9 (histogram
   // built during the sweep), 11 and 11 bits, then the order-preserving
-  // compaction (ties to the smaller id); the row is read back four times
-  // (two digit passes, counting, placing), in rounds of NT * V positions with
-  // V consecutive keys per thread (one 16-byte load when N % 4 == 0, so rows
-  // are 16-byte aligned; else V = 1).  Scratch reuses the K tiles' LDS: an
-  // 11-bit histogram, then the compaction's per-(round, wave) counts.
+  // compaction (ties to the smaller id); the row is read back three times
+  // (second digit; third digit with the counts; placing), or four when the
+  // keys sharing the threshold's first 20 bits do not fit in LDS, in rounds
+  // of NT * V positions with V consecutive keys per thread (one 16-byte load
+  // when N % 4 == 0, so rows are 16-byte aligned; else V = 1).  Scratch
+  // reuses the K tiles' LDS: an 11-bit histogram, the compaction's
+  // per-(round, wave) counts and the gathered keys.
   constexpr int NT = NW * 64;
   constexpr int H2 = 2048;
   static_assert(sizeof(lds_k) >= H2 * 4, "scratch for the 11-bit histogram");
   __shared__ uint32_t wtot[NW];
-  __shared__ uint32_t sel_digit, sel_below;
+  __shared__ uint32_t sel_digit, sel_below, cand_n;
   uint32_t* const sh = reinterpret_cast<uint32_t*>(lbase);
   const uint32_t* __restrict__ xr = reinterpret_cast<const uint32_t*>(mrow);
   int32_t* __restrict__ out = p.idx + ((size_t)hl * p.G + g) * p.K;
@@ -286,44 +288,95 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
     pick(std::integral_constant<int, H1>{}, h1, (uint32_t)p.K);
     uint32_t prefix = sel_digit << 22, pmask = 511u << 22;
     uint32_t remaining = (uint32_t)p.K - sel_below;
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 11 : 0;
-      for (int i = tid; i < H2; i += NT) sh[i] = 0u;
-      __syncthreads();
-      walk([&](int, int i0, const uint32_t (&u)[V]) {
+    // second digit (bits 21..11) among the keys that share the first
+    for (int i = tid; i < H2; i += NT) sh[i] = 0u;
+    __syncthreads();
+    walk([&](int, int i0, const uint32_t (&u)[V]) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const uint32_t key = mass_key31(u[e]);
-          if (i0 + e < N && (key & pmask) == prefix) atomicAdd(&sh[(key >> shift) & 2047u], 1u);
-        }
-      });
-      __syncthreads();
-      pick(std::integral_constant<int, H2>{}, sh, remaining);
-      prefix |= sel_digit << shift;
-      pmask |= 2047u << shift;
-      remaining -= sel_below;
-    }
-    const uint32_t T = prefix;
-    const uint32_t need = remaining;
+      for (int e = 0; e < V; ++e) {
+        const uint32_t key = mass_key31(u[e]);
+        if (i0 + e < N && (key & pmask) == prefix) atomicAdd(&sh[(key >> 11) & 2047u], 1u);
+      }
+    });
+    __syncthreads();
+    pick(std::integral_constant<int, H2>{}, sh, remaining);
+    prefix |= sel_digit << 11;
+    pmask |= 2047u << 11;
+    remaining -= sel_below;
 
-    // compaction, step 1: per round and wave, the keys below and equal to T
-    uint32_t* const cnt_lt = sh;
-    uint32_t* const cnt_eq = sh + rounds * NW;
+    // Third digit (bits 10..0).  The same read also counts, per round and
+    // wave, the keys whose first 20 bits are below the threshold's (all of
+    // them are below T) and gathers the few that share those bits, with their
+    // positions: once T is known they complete the counts, so no separate
+    // counting read is needed.  When the LDS has no room for them beside the
+    // histogram and the counts, or they do not fit, the counting read runs.
+    constexpr int WORDS = (int)(sizeof(lds_k) / 4);
+    const int cap = (WORDS - H2 - 2 * rounds * NW) / 2;        // (key, position) pairs
+    const bool merged = cap >= 64;
+    uint32_t* const cnt_lt = merged ? sh + H2 : sh;
+    uint32_t* const cnt_eq = cnt_lt + rounds * NW;
+    uint32_t* const cand = cnt_eq + rounds * NW;
+    for (int i = tid; i < H2; i += NT) sh[i] = 0u;
+    if (tid == 0) cand_n = 0u;
+    __syncthreads();
     walk([&](int r, int i0, const uint32_t (&u)[V]) {
-      uint32_t nlt = 0, neq = 0;
+      uint32_t nlt = 0;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const uint32_t key = mass_key31(u[e]);
         const bool valid = i0 + e < N;
-        nlt += (uint32_t)__popcll(__ballot(valid && key < T));
-        neq += (uint32_t)__popcll(__ballot(valid && key == T));
+        const bool c = valid && (key & pmask) == prefix;
+        if (c) atomicAdd(&sh[key & 2047u], 1u);
+        if (merged) {
+          nlt += (uint32_t)__popcll(__ballot(valid && (key & pmask) < prefix));
+          const uint64_t bc = __ballot(c);
+          uint32_t base = 0;
+          if (lane == 0 && bc) base = atomicAdd(&cand_n, (uint32_t)__popcll(bc));
+          base = __shfl(base, 0);
+          const uint32_t at = base + (uint32_t)__popcll(bc & lt_mask);
+          if (c && at < (uint32_t)cap) {
+            cand[2 * at] = key;
+            cand[2 * at + 1] = (uint32_t)(i0 + e);
+          }
+        }
       }
-      if (lane == 0) {
+      if (merged && lane == 0) {
         cnt_lt[r * NW + w] = nlt;
-        cnt_eq[r * NW + w] = neq;
+        cnt_eq[r * NW + w] = 0u;
       }
     });
+    __syncthreads();
+    const uint32_t ncand = cand_n;
+    pick(std::integral_constant<int, H2>{}, sh, remaining);
+    const uint32_t T = prefix | sel_digit;
+    const uint32_t need = remaining - sel_below;
+
+    if (merged && ncand <= (uint32_t)cap) {
+      // complete the counts with the gathered keys
+      for (uint32_t j = tid; j < ncand; j += NT) {
+        const uint32_t key = cand[2 * j], pos = cand[2 * j + 1];
+        const uint32_t r = pos / (NT * V), ww = (pos % (NT * V)) / (64 * V);
+        if (key < T) atomicAdd(&cnt_lt[r * NW + ww], 1u);
+        else if (key == T) atomicAdd(&cnt_eq[r * NW + ww], 1u);
+      }
+    } else {
+      // compaction, step 1 as its own read: per round and wave, the keys
+      // below and equal to T
+      walk([&](int r, int i0, const uint32_t (&u)[V]) {
+        uint32_t nlt = 0, neq = 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const uint32_t key = mass_key31(u[e]);
+          const bool valid = i0 + e < N;
+          nlt += (uint32_t)__popcll(__ballot(valid && key < T));
+          neq += (uint32_t)__popcll(__ballot(valid && key == T));
+        }
+        if (lane == 0) {
+          cnt_lt[r * NW + w] = nlt;
+          cnt_eq[r * NW + w] = neq;
+        }
+      });
+    }
     __syncthreads();
     // step 2: exclusive scans of both count arrays in position order (wave 0
     // scans the lt counts, wave 1 the eq counts; each lane owns a contiguous run)
