@@ -96,6 +96,16 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _like(t: torch.Tensor, name: str, dtype, shape, device) -> None:
+    """t must be a contiguous tensor of this dtype and shape on this device: the
+    kernels address it from the dimensions alone."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+
+
 def dims_of(q: torch.Tensor) -> Dims:
     B, H, N, D = q.shape
     return Dims(B, H, N, D)
@@ -127,21 +137,17 @@ def tokens_major(x: torch.Tensor) -> torch.Tensor:
 
 def _qkv(q, k, v=None):
     _need(q, "q", torch.bfloat16, 4)
-    _need(k, "k", torch.bfloat16, 4)
-    if k.shape != q.shape:
-        raise ValueError("q and k must have the same shape")
+    _like(k, "k", torch.bfloat16, q.shape, q.device)
     if v is not None:
-        _need(v, "v", torch.bfloat16, 4)
-        if v.shape != q.shape:
-            raise ValueError("q and v must have the same shape")
+        _like(v, "v", torch.bfloat16, q.shape, q.device)
 
 
 def _out(q, out, out_dtype):
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    _need(out, "out", out.dtype, 4)
-    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != tuple(q.shape):
-        raise ValueError("out must be bf16 or float32 with the shape of q")
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be a bf16 or float32 tensor")
+    _like(out, "out", out.dtype, q.shape, q.device)
     return out
 
 
@@ -155,6 +161,8 @@ def dense_attn(q, k, v, scale=None, want_lse=False, out=None, lse=None, out_dtyp
     out = _out(q, out, out_dtype)
     if want_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif want_lse:
+        _like(lse, "lse", torch.float32, (B, H, N), q.device)
     fn = _lib.mcs_dense_attn_f32out if out.dtype == torch.float32 else _lib.mcs_dense_attn
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if want_lse else None), dims_of(q), scale,
               _stream(q)))
@@ -167,13 +175,15 @@ def sparse_attn(q, k, v, perm, kv_idx, C, residual=None, scale=None, out=None, o
     The output is bf16 unless out (or out_dtype) is float32."""
     _qkv(q, k, v)
     B, H, N, D = q.shape
-    _need(perm, "perm", torch.int32, 3)
+    _like(perm, "perm", torch.int32, (B, H, N), q.device)
     _need(kv_idx, "kv_idx", torch.int32, 4)
     if residual is not None:
-        _need(residual, "residual", torch.bfloat16, 4)
+        _like(residual, "residual", torch.bfloat16, q.shape, q.device)
     G = num_groups(N, C)
     if tuple(kv_idx.shape[:3]) != (B, H, G):
         raise ValueError(f"kv_idx must be [B, H, G={G}, K] (got {tuple(kv_idx.shape)})")
+    if kv_idx.device != q.device:
+        raise ValueError(f"kv_idx must be on {q.device} (got {kv_idx.device})")
     K = kv_idx.shape[3]
     scale = default_scale(D) if scale is None else scale
     out = _out(q, out, out_dtype)
@@ -186,8 +196,9 @@ def sparse_attn(q, k, v, perm, kv_idx, C, residual=None, scale=None, out=None, o
 def residual_update(o_dense, o_sparse, out=None):
     """mcs_residual_update: bf16(o_dense - o_sparse)."""
     _need(o_dense, "o_dense", torch.bfloat16, o_dense.dim())
-    _need(o_sparse, "o_sparse", torch.bfloat16, o_sparse.dim())
+    _like(o_sparse, "o_sparse", torch.bfloat16, o_dense.shape, o_dense.device)
     out = torch.empty_like(o_dense) if out is None else out
+    _like(out, "out", torch.bfloat16, o_dense.shape, o_dense.device)
     _check(_lib.mcs_residual_update(_ptr(o_dense), _ptr(o_sparse), _ptr(out), o_dense.numel(),
                                     _stream(o_dense)))
     return out
@@ -212,12 +223,15 @@ def select_two_pass(q, k, lse, perm, C, K, scale=None, out=None, workspace=None,
 def _select(fn, q, k, lse, perm, C, K, scale, out, workspace, max_workspace_bytes):
     _qkv(q, k)
     B, H, N, D = q.shape
-    _need(lse, "lse", torch.float32, 3)
-    _need(perm, "perm", torch.int32, 3)
+    _like(lse, "lse", torch.float32, (B, H, N), q.device)
+    _like(perm, "perm", torch.int32, (B, H, N), q.device)
     scale = default_scale(D) if scale is None else scale
     G = num_groups(N, C)
     out = torch.empty((B, H, G, K), dtype=torch.int32, device=q.device) if out is None else out
-    if workspace is None:
+    _like(out, "out", torch.int32, (B, H, G, K), q.device)
+    if workspace is not None:
+        _like(workspace, "workspace", torch.uint8, (workspace.numel(),), q.device)
+    else:
         per_head = select_workspace_bytes(q.shape, C, K, all_heads=False)
         nbytes = min(select_workspace_bytes(q.shape, C, K), max(per_head, max_workspace_bytes // per_head * per_head))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -231,6 +245,7 @@ def topk(scores, K, out=None):
     _need(scores, "scores", torch.float32, 2)
     rows, n = scores.shape
     out = torch.empty((rows, K), dtype=torch.int32, device=scores.device) if out is None else out
+    _like(out, "out", torch.int32, (rows, K), scores.device)
     _check(_lib.mcs_topk(_ptr(scores), _ptr(out), rows, n, K, _stream(scores)))
     return out
 
@@ -244,8 +259,11 @@ def group(q, C, power_iters=0, out=None, workspace=None):
     _need(q, "q", torch.bfloat16, 4)
     B, H, N, D = q.shape
     out = torch.empty((B, H, N), dtype=torch.int32, device=q.device) if out is None else out
+    _like(out, "out", torch.int32, (B, H, N), q.device)
     if workspace is None:
         workspace = torch.empty(max(group_workspace_bytes(q.shape, C), 16), dtype=torch.uint8, device=q.device)
+    else:
+        _like(workspace, "workspace", torch.uint8, (workspace.numel(),), q.device)
     _check(_lib.mcs_group(_ptr(q), _ptr(out), dims_of(q), C, power_iters, _ptr(workspace),
                           workspace.numel(), _stream(q)))
     return out
