@@ -196,7 +196,6 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   __shared__ float sred[MSTEP / 4][D];
   __shared__ float part[2][RB][D];
   __shared__ float mu[D], vec[D];
-  __shared__ float red[4];
   __shared__ int ish[2];
   const int slot = blockIdx.x, bh = blockIdx.y;
   int off, n, g;
