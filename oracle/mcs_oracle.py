@@ -33,17 +33,18 @@ Readings of points the pages leave open:
   R2 no mask: every query sees all N keys (bidirectional DiT attention);
   R3 top-K ties: larger mass first, equal mass -> smaller KV id; output ascending;
   R4 sparse softmax renormalises over the selected set;
-  R5 PDDP split at rank C*floor(g/2) of the ordering by (projection, query id),
-     with g = ceil(n/C) groups in the node; the exact split is the median when g
-     is even and n = g*C; the remainder group ends up rightmost;
+  R5 PDDP split at rank C*floor(g/2) of the projection order, with g =
+     ceil(n/C) groups in the node; the exact split is the median when g is
+     even and n = g*C; the remainder group ends up rightmost;
   R6 principal direction sign: largest-|.| component positive (ties -> lowest id);
-  R6b the principal direction of a PDDP node comes from power iteration, the
+  R6b equal projections are ordered by query id;
+  R7 the residual is O_dense - O_sparse formed at the anchor with the anchor's
+     own Q, K, V and the freshly built groups and indices;
+  R8 the principal direction of a PDDP node comes from power iteration, the
      pages' algorithm for Fast PDDP (ai.info "Key Contributions": batched power
      iteration): 32 steps on the node covariance, started from its column of
      largest diagonal, normalised every step (the pages give neither count nor
-     start); mode="eigh" gives the exact eigenvector instead;
-  R7 the residual is O_dense - O_sparse formed at the anchor with the anchor's
-     own Q, K, V and the freshly built groups and indices.
+     start); mode="eigh" gives the exact eigenvector instead.
 
 Pins (what ties each function to something other than itself) live in
 ``tests/test_oracle_*.py``; every function below is pinned there.
@@ -271,9 +272,9 @@ def pddp(q, C: int, mode: str = "power", power_iters: int = 32) -> np.ndarray:
 
     Node with ids I (n = |I|, g = ceil(n/C) groups): a leaf when g == 1;
     otherwise order I by (projection on the node's principal direction, query
-    id), left child = first C*floor(g/2) ids, right child = the rest (R5).
+    id (R6b)), left child = first C*floor(g/2) ids, right child = the rest (R5).
     Leaves are emitted left-first, so perm[g*C:(g+1)*C] is group g.  The
-    direction comes from power iteration by default (R6b), or from eigh.
+    direction comes from power iteration by default (R8), or from eigh.
     Returns perm [N].
     """
     q = _f64(q)
