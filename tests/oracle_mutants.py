@@ -66,6 +66,25 @@ MUTANTS = {
     "token_oracle_smallest_mass": (DIAG, '"token_oracle": _top_ids(mass, K),', '"token_oracle": _top_ids(-mass, K),'),
     "kmeans_farthest_centre": (DIAG, "labels = np.argmin(d, axis=1)", "labels = np.argmax(d, axis=1)"),
     "inflation_rounds_down": (DIAG, "(-(-sizes // tile) * tile)", "((sizes // tile) * tile)"),
+    "pddp_ties_to_larger_id": (MCS, "order = np.lexsort((ids, proj))", "order = np.lexsort((-ids, proj))"),
+    "pddp_right_child_first": (MCS, "        split(ids[order[:r]])\n        split(ids[order[r:]])\n",
+                               "        split(ids[order[r:]])\n        split(ids[order[:r]])\n"),
+    "variance_global_mean": (MCS, "total += float(((x - x.mean(axis=0)) ** 2).sum())",
+                             "total += float(((x - q.mean(axis=0)) ** 2).sum())"),
+    "dense_keys_as_values": (MCS, "out[r0:r0 + ROW_BLOCK] = (e / z) @ v", "out[r0:r0 + ROW_BLOCK] = (e / z) @ k"),
+    "mass_lse_unpermuted": (MCS, "probabilities(q[members], k, lse[members], scale).sum(axis=0)",
+                            "probabilities(q[members], k, lse[:len(members)], scale).sum(axis=0)"),
+    "sparse_queries_unpermuted": (MCS, "s = attention_scores(q[members], k[sel], scale)",
+                                  "s = attention_scores(q[:len(members)], k[sel], scale)"),
+    "sign_uses_max_not_abs": (MCS, "i = int(np.argmax(np.abs(vec)))", "i = int(np.argmax(vec))"),
+    "projection_on_the_mean": (MCS, "proj = (q[ids] - mu) @ vec", "proj = (q[ids] - mu) @ mu"),
+    "pooled_query_sum_over_all": (DIAG, "pooled = scale * (kbar @ q[rows].mean(axis=0))",
+                                  "pooled = scale * (kbar @ q.mean(axis=0))"),
+    "block_oracle_uses_first_block": (DIAG, '"block_oracle": _block_keys(_top_ids(bmass, nblk), N),',
+                                      '"block_oracle": _block_keys(np.arange(nblk), N),'),
+    "perquery_ties_to_larger_id": (DIAG, "keep = gt | (eq & (np.cumsum(eq, axis=1) <= need))",
+                                   "keep = gt | (eq & (np.cumsum(eq[:, ::-1], axis=1)[:, ::-1] <= need))"),
+    "rel_l1_over_kept_total": (DIAG, "total = np.abs(o_held).sum()", "total = np.abs(o_held).sum() / Nq"),
 }
 
 

@@ -176,11 +176,17 @@ def test_budgets_in_one_call_equal_separate_calls_and_kmeans_groups_keep_the_ord
         assert r_["block_oracle"]["recall"] >= r_["mean_pooled_block"]["recall"] - 1e-12
 
 
-def test_per_query_oracle_equals_brute_force_masking():
+@pytest.mark.parametrize("dup", [False, True])
+def test_per_query_oracle_equals_brute_force_masking(dup):
     # every row keeps its K largest probabilities; recall and output error
-    # recomputed here from a dense mask and a plain product, several budgets
+    # recomputed here from a dense mask and a plain product, several budgets.
+    # dup: keys repeated in pairs, so every probability ties with its twin and
+    # the rule for a tie at the K-th value (smaller key id kept) decides which
+    # value row enters the output (the value rows stay distinct)
     N, C = 300, 64
     q, k, v = _head(N, 8, 31)
+    if dup:
+        k[1::2] = k[0::2]
     scale = 0.5
     groups = dg.groups_from_perm(np.random.default_rng(32).permutation(N), C)
     Ks = [1, 37, 128, 299, 300]
@@ -196,6 +202,26 @@ def test_per_query_oracle_equals_brute_force_masking():
         assert got[K]["per_query_oracle"]["recall"] == pytest.approx(kept.mean(), rel=1e-12)
         err = np.abs(pm @ v / kept[:, None] - o).sum() / np.abs(o).sum()
         assert got[K]["per_query_oracle"]["rel_l1"] == pytest.approx(err, rel=1e-10, abs=1e-14)
+
+
+def test_mean_pooling_uses_each_groups_own_mean_query():
+    # two groups that prefer different key blocks: group A points at block 0,
+    # group B (fewer, shorter queries) at block 1.  Pooling each group's own
+    # mean query picks each group's block, as the block oracle does; the mean
+    # over all queries would point both groups at block 0
+    r = np.random.default_rng(51)
+    D, B = 4, dg.KV_BLOCK
+    e = np.eye(D)
+    k = np.concatenate([3 * e[0] + 0.05 * r.standard_normal((B, D)),
+                        3 * e[1] + 0.05 * r.standard_normal((B, D))])
+    v = r.standard_normal((2 * B, D))
+    q = np.concatenate([2 * e[0] + 0.05 * r.standard_normal((96, D)),
+                        1.5 * e[1] + 0.05 * r.standard_normal((32, D))])
+    groups = [np.arange(96), np.arange(96, 128)]
+    got = dg.diagnose_groups(q, k, v, groups, [B], 1.0)[B]
+    assert got["mean_pooled_block"]["recall"] == pytest.approx(got["block_oracle"]["recall"], rel=1e-12)
+    assert got["mean_pooled_block"]["rel_l1"] == pytest.approx(got["block_oracle"]["rel_l1"], rel=1e-12)
+    assert got["mean_pooled_block"]["recall"] > 0.95
 
 
 def test_scoring_a_sample_of_groups_averages_over_their_queries():
