@@ -138,14 +138,15 @@ def test_select_with_gpu_lse(mcs):
 @pytest.mark.parametrize("N,D,C,K,dup", [(4097, 128, 128, 800, False), (3000, 64, 64, 1500, True),
                                          (3001, 128, 64, 2999, True), (75600, 128, 128, 15104, False),
                                          (131072, 64, 128, 26215, False), (131073, 64, 128, 100, False),
-                                         (131071, 64, 128, 5000, False), (65536, 128, 64, 65536, False)])
+                                         (131071, 64, 128, 5000, False), (65536, 128, 64, 65536, False),
+                                         (262144, 128, 128, 4096, False), (262145, 128, 128, 4096, False)])
 def test_fused_select_equals_two_pass(mcs, N, D, C, K, dup):
     """One head per case, LSE from the GPU's own dense pass: a large-workload
     head, the largest rows the fused kernel holds for D = 64 (16-byte and
     4-byte reads; the latter leaves no LDS for the gathered third-digit keys,
-    so the counting read runs) and one past it (mcs_select takes the
-    two-kernel route), K = N, and duplicated keys (equal masses in pairs, so
-    the tie rule decides at the K-th key)."""
+    so the counting read runs) and for D = 128, one past each (mcs_select takes
+    the two-kernel route), K = N, and duplicated keys (equal masses in pairs,
+    so the tie rule decides at the K-th key)."""
     q = synth.gaussian((1, 1, N, D), 60 + N, 1.5)
     k = synth.gaussian((1, 1, N, D), 61 + N, 1.5)
     if dup:
