@@ -165,3 +165,24 @@ def test_layout_helpers_round_trip():
     assert torch.equal(y[1, 2, 4], x[1, 4, 2])
     z = binding.tokens_major(y)
     assert z.is_contiguous() and torch.equal(z, x)
+
+
+def test_header_is_plain_c_and_links(lib, tmp_path):
+    """include/mcs.h is a C header: a C99 program includes it, links against
+    the library and calls a host-only query (no GPU work)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "use_mcs.c"
+    src.write_text('#include "mcs.h"\n'
+                   "int main(void) {\n"
+                   "  mcs_dims d = {1, 2, 1000, 128};\n"
+                   "  return mcs_select_workspace(d, 128, 100) == 8 * 1000 * 4 && mcs_version() == MCS_VERSION ? 0 : 1;\n"
+                   "}\n")
+    lib_dir = os.path.join(root, "token_sparse_attention_amd")
+    exe = tmp_path / "use_mcs"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(root, "include"),
+                    str(src), "-L", lib_dir, "-lmcs", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0
