@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MCS_VERSION 101
+#define MCS_VERSION 200
 
 #if defined(__GNUC__)
 #define MCS_API __attribute__((visibility("default")))
@@ -86,8 +86,9 @@ typedef struct {
 /*
  * Dense attention with row log-sum-exp: the first pass of the two-pass exact
  * selector and the anchor step's output (ai.info, "Methodology in Plain
- * English": the first pass computes the dense output and row-wise
- * log-sum-exp values).  Also the build's own dense baseline.
+ * English": pass one of the selector yields the attention output together
+ * with one log-sum-exp per query row).  Also the library's own dense
+ * baseline.
  *   o[b,h,i,:] = sum_j softmax_j(scale * q_i.k_j) v_j   (no mask)
  *   lse[b,h,i] = ln sum_j exp(scale * q_i.k_j)          (if lse != NULL)
  * In: q, k, v bf16 [B,H,N,D].  Out: o bf16 [B,H,N,D]; lse float32 [B,H,N] or
@@ -189,23 +190,27 @@ MCS_API mcs_status mcs_topk(const float* scores, int32_t* idx, int64_t rows, int
 /*
  * Median-split PDDP grouping (ai.info, "Key Contributions" and "Methodology in
  * Plain English"; wispaper.ai, "Token-level selection needs tile-aligned query
- * groups": recursively project each group on its principal direction and
- * split the ordered queries at the median until every group holds exactly C
- * queries; batched power iteration over all heads at each tree depth).
+ * groups": each node's queries are projected on the node's principal
+ * direction and cut at the median, recursively, until every group holds
+ * exactly C queries; the directions of all nodes of a tree depth are found
+ * together, by batched power iteration on the pages).
  * Per head, a node of n queries forms g = ceil(n/C) groups; if g > 1 its
  * queries are ordered by (projection on the node's principal direction, query
  * id) and the first C*floor(g/2) form the left child, the rest the right
  * child.  Leaves are written left-first, so group g is perm[g*C ..].  The
- * principal direction comes from power_iters steps of power iteration on the
- * node's covariance (power_iters <= 0 selects the default, 32), started from
- * the covariance column of largest diagonal, sign fixed so that its
- * largest-magnitude component is positive.  Covariance, power iteration and
- * projections are fp32.
+ * principal direction is the top eigenvector of the node's covariance, sign
+ * fixed so that its largest-magnitude component is positive.  It is computed
+ * by Lanczos with full reorthogonalisation (the Krylov form of power
+ * iteration: the same matrix-vector products, but it converges where power
+ * steps stall on nearly equal leading eigenvalues), started from the
+ * covariance column of largest diagonal, for lanczos_steps steps
+ * (<= 0 selects the default, 32; at most 64).  Covariance, Lanczos and
+ * projections are fp32; the small tridiagonal eigenproblem is fp64.
  * In: q bf16 [B,H,N,D].  Out: perm int32 [B,H,N].  ws: device workspace of at
  * least mcs_group_workspace(d, C) bytes.
  */
 MCS_API mcs_status mcs_group(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C,
-                     int32_t power_iters, void* ws, size_t ws_bytes, void* stream);
+                     int32_t lanczos_steps, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace of mcs_group in bytes (per-query projections and ids, per-node
  * directions, and partial moments of the large nodes near the root). */

@@ -40,11 +40,13 @@ Readings of points the pages leave open:
   R6b equal projections are ordered by query id;
   R7 the residual is O_dense - O_sparse formed at the anchor with the anchor's
      own Q, K, V and the freshly built groups and indices;
-  R8 the principal direction of a PDDP node comes from power iteration, the
-     pages' algorithm for Fast PDDP (ai.info "Key Contributions": batched power
-     iteration): 32 steps on the node covariance, started from its column of
-     largest diagonal, normalised every step (the pages give neither count nor
-     start); mode="eigh" gives the exact eigenvector instead.
+  R8 the principal direction of a PDDP node is what the term means: the
+     eigenvector of the largest eigenvalue of the node's covariance (exact,
+     from numpy's symmetric eigensolver, the default).  The pages compute it
+     by batched power iteration (ai.info "Key Contributions") but give no step
+     count or start, so a fixed number of power steps is no definition of it;
+     mode="power" runs such steps from the covariance column of largest
+     diagonal, as a mirror of the iteration for tests.
 
 Pins (what ties each function to something other than itself) live in
 ``tests/test_oracle_*.py``; every function below is pinned there.
@@ -75,8 +77,8 @@ def _f64(x) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # Dense attention with row log-sum-exp
-# [ai.info "Methodology in Plain English": the first selection pass computes
-#  the dense output and the row-wise log-sum-exp values]
+# [ai.info "Methodology in Plain English": pass one of the selector yields the
+#  attention output together with one log-sum-exp per query row]
 # ---------------------------------------------------------------------------
 
 def attention_scores(q, k, scale: float) -> np.ndarray:
@@ -198,7 +200,7 @@ def residual(o_dense, o_sparse) -> np.ndarray:
     return _f64(o_dense) - _f64(o_sparse)
 
 
-def anchor_step(q, k, v, C: int, K: int, scale: float, pddp_mode: str = "power",
+def anchor_step(q, k, v, C: int, K: int, scale: float, pddp_mode: str = "eigh",
                 power_iters: int = 32):
     """One anchor step of one head, in the pages' order.
 
@@ -267,14 +269,15 @@ def principal_direction(x, mode: str = "eigh", power_iters: int = 16):
     return mu, _canonical_sign(vec)
 
 
-def pddp(q, C: int, mode: str = "power", power_iters: int = 32) -> np.ndarray:
+def pddp(q, C: int, mode: str = "eigh", power_iters: int = 32) -> np.ndarray:
     """Median-split PDDP of one head's queries into exactly-C groups.
 
     Node with ids I (n = |I|, g = ceil(n/C) groups): a leaf when g == 1;
     otherwise order I by (projection on the node's principal direction, query
     id (R6b)), left child = first C*floor(g/2) ids, right child = the rest (R5).
     Leaves are emitted left-first, so perm[g*C:(g+1)*C] is group g.  The
-    direction comes from power iteration by default (R8), or from eigh.
+    direction is the exact top eigenvector by default (R8); mode="power"
+    takes power_iters power steps instead.
     Returns perm [N].
     """
     q = _f64(q)
@@ -347,7 +350,7 @@ def select_bh(q, k, lse, perm, C: int, K: int, scale: float):
     return idx, mass
 
 
-def pddp_bh(q, C: int, mode: str = "power", power_iters: int = 32) -> np.ndarray:
+def pddp_bh(q, C: int, mode: str = "eigh", power_iters: int = 32) -> np.ndarray:
     qs, bh = _heads(q)
     perms = [pddp(qs[i], C, mode=mode, power_iters=power_iters) for i in range(qs.shape[0])]
     return np.stack(perms).reshape(bh + perms[0].shape)

@@ -53,7 +53,7 @@ MUTANTS = {
     "reuse_subtracts_residual": (MCS, "out = out + _f64(residual)", "out = out - _f64(residual)"),
     "lse_log2": (MCS, "lse[r0:r0 + ROW_BLOCK] = (m + np.log(z))[:, 0]",
                  "lse[r0:r0 + ROW_BLOCK] = (m + np.log2(z))[:, 0]"),
-    "pddp_default_eigh": (MCS, 'def pddp(q, C: int, mode: str = "power"', 'def pddp(q, C: int, mode: str = "eigh"'),
+    "pddp_default_power": (MCS, 'def pddp(q, C: int, mode: str = "eigh"', 'def pddp(q, C: int, mode: str = "power"'),
     "retained_mass_first_ids": (MCS, "mass[g, np.asarray(idx[g])].sum()", "mass[g, :len(idx[g])].sum()"),
     "block_keys_off_by_one": (DIAG, "keys = (blocks[:, None] * KV_BLOCK + np.arange(KV_BLOCK)[None, :]).ravel()",
                               "keys = (blocks[:, None] * KV_BLOCK + 1 + np.arange(KV_BLOCK)[None, :]).ravel()"),

@@ -138,7 +138,7 @@ def test_select_group_topk_residual_validation(lib):
     gws = lib.mcs_group_workspace(d, 128)
     assert gws >= 2 * 2 * 1000 * 4
     assert lib.mcs_group(A, B_, d, 128, 0, 0x80000, gws - 1, None) == c["MCS_E_WORKSPACE"]
-    assert lib.mcs_group(A, B_, d, 128, 5000, 0x80000, gws, None) == c["MCS_E_ARG"]
+    assert lib.mcs_group(A, B_, d, 128, 65, 0x80000, gws, None) == c["MCS_E_ARG"]    # lanczos_steps <= 64
     assert lib.mcs_group(A, B_, d, 100, 0, 0x80000, gws, None) == c["MCS_E_GROUP_SIZE"]
     assert lib.mcs_group_workspace(Dims(1, 2, 1000, 128), 100) == 0
     assert lib.mcs_topk(A, B_, 0, 10, 5, None) == c["MCS_E_SHAPE"]

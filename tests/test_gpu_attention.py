@@ -145,6 +145,44 @@ def test_residual_update_exact(mcs):
     np.testing.assert_array_equal(got, expect)
 
 
+@pytest.mark.parametrize("alias", ["o_dense", "o_sparse"])
+def test_residual_update_in_place(mcs, alias):
+    # 3090 elements: 386 16-byte vectors and a 2-element tail
+    a = synth.gaussian((2, 3, 515), seed=23)
+    b = synth.gaussian((2, 3, 515), seed=24, scale=0.5)
+    expect = synth.to_bf16_bits((synth.to_f32(a) - synth.to_f32(b)).astype(np.float32))
+    da, db = to_dev_bf16(a), to_dev_bf16(b)
+    out = da if alias == "o_dense" else db
+    r = mcs.residual_update(da, db, out=out)
+    assert r.data_ptr() == out.data_ptr()
+    np.testing.assert_array_equal(r.view(torch.int16).cpu().numpy().view(np.uint16), expect)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_sparse_out_of_range_ids_read_zero_rows(mcs, D):
+    # ids past N, far past N (id * row bytes would wrap 32 bits) and negative
+    # ids each read a zero key and value row
+    B, H, N, C, K = 1, 1, 300, 128, 70
+    q, k, v = _qkv(B, H, N, D, seed=41, scale=1.5)
+    G = accounting.num_groups(N, C)
+    perm = synth.random_perm(B, H, N, seed=42)
+    idx = synth.random_index_sets(B, H, G, K, N, seed=43)
+    bad = idx.copy()
+    wrap = 2 ** 32 // (2 * D)             # id whose row offset wraps to 0 in 32 bits
+    bad[0, 0, 0, 5] = N
+    bad[0, 0, 0, 6] = wrap + 3
+    bad[0, 0, 1, 7] = -1
+    bad[0, 0, 2, 9] = 2 ** 31 - 1
+    bad[0, 0, 2, 10] = -2 ** 31
+    o = mcs.sparse_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), to_dev(perm), to_dev(bad), C,
+                        out_dtype=torch.float32)
+    kz = np.concatenate([synth.to_f64(k), np.zeros((B, H, 1, D))], axis=2)
+    vz = np.concatenate([synth.to_f64(v), np.zeros((B, H, 1, D))], axis=2)
+    mapped = np.where((bad >= 0) & (bad < N), bad, N)
+    ref = oracle.sparse_attention_bh(synth.to_f64(q), kz, vz, perm, mapped, C, 1 / math.sqrt(D))
+    assert_output_close(o.cpu().numpy(), ref, "sparse O with out-of-range ids")
+
+
 def test_anchor_identity_on_gpu(mcs):
     # with the anchor's own inputs, sparse + residual reproduces the dense output
     B, H, N, D, C, K = 1, 2, 640, 64, 64, 128

@@ -2,7 +2,8 @@
 
 Group sizes must match exactly (a permutation, groups of C, one short last
 group by construction of perm), and the within-group variance W of the GPU's
-grouping must be within 1% of the oracle's (exact eigenvectors).  Closed-form
+grouping must be within 1% of the oracle's, which splits on exact
+eigenvectors (the principal directions).  Closed-form
 cases (collinear queries, identical queries, separated clusters) must match
 exactly, and collinear queries with repeated values at ragged sizes (a short
 remainder group, one group, N < C) must give the oracle's groups exactly.
@@ -71,14 +72,35 @@ def test_within_group_variance_within_one_percent(mcs, name, N, heads):
         assert abs(w_gpu - w_ref) <= 0.01 * w_ref, (w_gpu, w_ref)
 
 
-def test_power_iteration_count_argument(mcs):
+def test_lanczos_steps_argument(mcs):
     x = synth.generate("tiny", heads=[(0, 0)])
     dq = to_dev_bf16(x["q"])
-    a = mcs.group(dq, 64, power_iters=0).cpu().numpy()
-    b = mcs.group(dq, 64, power_iters=32).cpu().numpy()
-    c = mcs.group(dq, 64, power_iters=64).cpu().numpy()
+    a = mcs.group(dq, 64, lanczos_steps=0).cpu().numpy()
+    b = mcs.group(dq, 64, lanczos_steps=32).cpu().numpy()
     np.testing.assert_array_equal(a, b)          # 0 selects the default (32)
-    assert_perm(c)
+    for steps in (1, 2, 5, 64):
+        assert_perm(mcs.group(dq, 64, lanczos_steps=steps).cpu().numpy())
+    with pytest.raises(mcs.McsError):
+        mcs.group(dq, 64, lanczos_steps=65)
+
+
+@pytest.mark.parametrize("steps", [32, 64])
+def test_clustered_heads_match_exact_eigenvectors(mcs, steps):
+    # clustered heads have nearly equal leading eigenvalues in many nodes, where
+    # a fixed number of power steps would not converge; at 32 and 64 Lanczos
+    # steps W must stay within 1% of the exact-eigenvector split
+    name = "asset3d"
+    w = synth.WORKLOADS[name]
+    x = synth.generate(name, heads=[(0, h) for h in (3, 8, 14)])
+    q = np.ascontiguousarray(x["q"][:, :, :12288])
+    perm = mcs.group(to_dev_bf16(q), w.C, lanczos_steps=steps).cpu().numpy()
+    assert_perm(perm)
+    qf = synth.to_f64(q)
+    for h in range(3):
+        ref = oracle.pddp(qf[0, h], w.C)
+        w_ref = oracle.within_group_variance(qf[0, h], ref, w.C)
+        w_gpu = within_group_variance(qf[0, h], perm[0, h], w.C)
+        assert abs(w_gpu - w_ref) <= 0.01 * w_ref, (h, w_gpu, w_ref)
 
 
 def test_deterministic(mcs):

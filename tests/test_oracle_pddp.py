@@ -91,19 +91,39 @@ def test_refinement_and_variance_monotone():
     assert prev_w < total
 
 
-def test_default_direction_is_power_iteration():
-    # power iteration (the pages' Fast PDDP) is the default; eigh stays available
-    q = _rand((300, 6), 21) * np.array([3.0, 2.9, 1.0, 0.5, 0.3, 0.1])
-    assert np.array_equal(oracle.pddp(q, 16), oracle.pddp(q, 16, mode="power", power_iters=32))
+def _known_covariance_points(n, lam, rot):
+    """n points with mean 0 and covariance exactly rot @ diag(lam) @ rot.T:
+    orthonormal columns scaled by sqrt(n * lam), rotated."""
+    z, _ = np.linalg.qr(np.random.default_rng(5).standard_normal((n, len(lam))))
+    z -= z.mean(axis=0)                        # still orthogonal columns after re-orthonormalising
+    z, _ = np.linalg.qr(z)
+    return (z * np.sqrt(n * np.asarray(lam))) @ rot.T, z
+
+
+def test_default_direction_is_the_exact_eigenvector():
+    # Covariance rot diag(1, 0.97, 0.3) rot^T by construction: the principal
+    # direction is rot[:, 0] (closed form), so the root splits the points by
+    # their first coordinate z[:, 0] in the eigenbasis.  Two leading variances
+    # 3% apart: 32 power steps from the largest-diagonal column stay far from
+    # rot[:, 0] and split differently, so this pins the default to the exact
+    # eigenvector and not to any fixed number of power steps.
+    c, s_ = np.cos(0.7), np.sin(0.7)
+    rot = np.array([[c, -s_, 0.0], [s_, c, 0.0], [0.0, 0.0, 1.0]]) @ \
+        np.array([[1.0, 0.0, 0.0], [0.0, np.cos(0.4), -np.sin(0.4)], [0.0, np.sin(0.4), np.cos(0.4)]])
+    q, z = _known_covariance_points(256, [1.0, 0.97, 0.3], rot)
+    np.testing.assert_allclose(np.cov(q.T, bias=True), rot @ np.diag([1.0, 0.97, 0.3]) @ rot.T, atol=1e-12)
+    u = rot[:, 0] if rot[np.argmax(np.abs(rot[:, 0])), 0] > 0 else -rot[:, 0]
+    _, v = oracle.principal_direction(q)
+    np.testing.assert_allclose(v, u, atol=1e-10)
+    proj = q @ u
+    left = set(np.argsort(proj, kind="stable")[:128].tolist())
+    perm = oracle.pddp(q, 32)
+    assert set(perm[:128].tolist()) == left
+    # a fixed number of power steps is a different (unconverged) reading here
+    perm_p = oracle.pddp(q, 32, mode="power", power_iters=32)
+    assert set(perm_p[:128].tolist()) != left
     for mode in ("eigh", "power"):
-        perm = oracle.pddp(q, 16, mode=mode)
-        assert sorted(perm.tolist()) == list(range(300))
-    # two leading variances 3% apart: 32 steps leave the direction short of the
-    # eigenvector, so the default must group differently from exact eigenvectors
-    q = _rand((256, 3), 0) * np.array([1.0, 0.97, 0.3])
-    sets = lambda perm: {frozenset(g.tolist()) for g in oracle.groups_from_perm(perm, 32)}
-    assert sets(oracle.pddp(q, 32, mode="eigh")) != sets(oracle.pddp(q, 32, mode="power"))
-    assert np.array_equal(oracle.pddp(q, 32), oracle.pddp(q, 32, mode="power", power_iters=32))
+        assert sorted(oracle.pddp(q, 16, mode=mode).tolist()) == list(range(256))
 
 
 def test_power_mode_with_many_steps_matches_eigh_grouping():

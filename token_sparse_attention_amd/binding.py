@@ -254,7 +254,7 @@ def group_workspace_bytes(q_shape, C) -> int:
     return int(_lib.mcs_group_workspace(Dims(*q_shape), C))
 
 
-def group(q, C, power_iters=0, out=None, workspace=None):
+def group(q, C, lanczos_steps=0, out=None, workspace=None):
     """mcs_group: median-split PDDP -> perm int32 [B, H, N]."""
     _need(q, "q", torch.bfloat16, 4)
     B, H, N, D = q.shape
@@ -264,14 +264,14 @@ def group(q, C, power_iters=0, out=None, workspace=None):
         workspace = torch.empty(max(group_workspace_bytes(q.shape, C), 16), dtype=torch.uint8, device=q.device)
     else:
         _like(workspace, "workspace", torch.uint8, (workspace.numel(),), q.device)
-    _check(_lib.mcs_group(_ptr(q), _ptr(out), dims_of(q), C, power_iters, _ptr(workspace),
+    _check(_lib.mcs_group(_ptr(q), _ptr(out), dims_of(q), C, lanczos_steps, _ptr(workspace),
                           workspace.numel(), _stream(q)))
     return out
 
 
-def anchor_step(q, k, v, C, K, scale=None, power_iters=0):
+def anchor_step(q, k, v, C, K, scale=None, lanczos_steps=0):
     """Anchor step: group, dense + LSE, select, sparse, residual.  Output is the dense output."""
-    perm = group(q, C, power_iters)
+    perm = group(q, C, lanczos_steps)
     o_dense, lse = dense_attn(q, k, v, scale, want_lse=True)
     kv_idx = select(q, k, lse, perm, C, K, scale)
     o_sparse = sparse_attn(q, k, v, perm, kv_idx, C, scale=scale)

@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -34,19 +35,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmcs)")
 
 
-def build(verbose: bool = False) -> str:
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), *sources, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object (in parallel), then links libmcs.so."""
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in sources]
+    cmds = [[hipcc(), *compile_flags, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+            for src, obj in zip(sources, objs)]
+    with ThreadPoolExecutor(max(1, min(len(cmds), os.cpu_count() or 1, 8))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), *FLAGS, *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

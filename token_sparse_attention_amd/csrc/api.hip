@@ -241,7 +241,7 @@ size_t mcs_group_workspace(mcs_dims d, int32_t C) {
   return mcs::plan_group(d.B * d.H, d.N, d.D, C).bytes;
 }
 
-mcs_status mcs_group(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C, int32_t power_iters,
+mcs_status mcs_group(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C, int32_t lanczos_steps,
                      void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "mcs_group";
   REQUIRE_PTR(q);
@@ -249,13 +249,14 @@ mcs_status mcs_group(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C, in
   mcs_status st;
   if ((st = check_dims(fn, d)) != MCS_OK) return st;
   if ((st = check_group_size(fn, C)) != MCS_OK) return st;
-  if (power_iters > 1000) return fail(MCS_E_ARG, "%s: power_iters must be <= 1000 (got %d)", fn, power_iters);
+  if (lanczos_steps > 64)
+    return fail(MCS_E_ARG, "%s: lanczos_steps must be <= 64 (got %d)", fn, lanczos_steps);
   const mcs::GroupPlan plan = mcs::plan_group(d.B * d.H, d.N, d.D, C);
   if (ws == nullptr || ws_bytes < plan.bytes)
     return fail(MCS_E_WORKSPACE, "%s: workspace of %zu bytes given, at least %zu needed", fn,
                 ws == nullptr ? (size_t)0 : ws_bytes, plan.bytes);
   if (!aligned16(ws)) return fail(MCS_E_ALIGN, "%s: ws is not 16-byte aligned", fn);
-  return launched(fn, mcs::run_group(q, perm, d.B * d.H, d.N, d.D, C, power_iters, ws, plan,
+  return launched(fn, mcs::run_group(q, perm, d.B * d.H, d.N, d.D, C, lanczos_steps, ws, plan,
                                      (hipStream_t)stream));
 }
 

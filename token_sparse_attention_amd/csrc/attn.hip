@@ -143,7 +143,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
       int row;
       if (SPARSE) row = ring[(tile % (2 * IDS_CHUNK)) * KT + r];
       else row = kp < nkeys ? kp : -1;   // -1: past the end -> zero rows
-      rowoff[j] = (uint32_t)row * (uint32_t)ROWB + coff[j];
+      // an id outside [0, N) gets an offset past the descriptor's end (N*D*2 <
+      // 2^31), so it reads a zero row; the product would wrap for large ids
+      rowoff[j] = (uint32_t)row < (uint32_t)p.N ? (uint32_t)row * (uint32_t)ROWB + coff[j] : 0x80000000u;
     }
   };
   // refill ring half (chunk & 1) with the ids of tiles [chunk*IDS_CHUNK, +IDS_CHUNK)

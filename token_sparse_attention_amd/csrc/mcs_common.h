@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mcs {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -79,6 +81,28 @@ __device__ __forceinline__ float halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   // IEEE addition is commutative, so both lanes of a pair get the same sum.
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the 64 lanes of a wave.  Every step pairs each lane with a partner
+// under a permutation that is its own inverse (xor 1, xor 2, mirror within 8
+// and within 16 lanes, xor 16, xor 32), so both lanes of a pair add the same
+// two values and every lane ends with bitwise the same total.
+__device__ __forceinline__ float wave_sum(float x) {
+  auto dpp = [](float v, auto ctrl_c) {
+    constexpr int CTRL = decltype(ctrl_c)::value;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+  x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));   // lane ^ 16
+  return halves_sum(x);
+}
+
+// A value that is the same in every lane, moved to a scalar register.
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
 __device__ __forceinline__ int clamp_id(int v, int n) { return v < 0 ? 0 : (v >= n ? n - 1 : v); }

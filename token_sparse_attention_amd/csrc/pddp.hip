@@ -4,9 +4,11 @@
 // wispaper.ai explainer ("Token-level selection needs tile-aligned query
 // groups") describe the grouping: project each node's queries on the node's
 // principal direction and split the ordered queries at the median, recursively,
-// until every group holds exactly C queries; the GPU version runs batched power
-// iteration over all heads at one tree depth at a time and passes only index
-// arrays between depths.
+// until every group holds exactly C queries; the GPU version finds the
+// directions of all nodes of all heads at one tree depth at once (the pages'
+// batched power iteration, here in its Krylov form: Lanczos on the same
+// matrix-vector products, which converges where plain power steps stall on a
+// small eigenvalue gap) and passes only index arrays between depths.
 //
 // Tree shape.  A node of n queries forms g = ceil(n/C) groups; a node with
 // g > 1 sends the first C*floor(g/2) queries (in projection order) left and the
@@ -21,9 +23,9 @@
 //   pddp_moments   (large nodes only) chunks of 2048 queries -> partial
 //                  sum(x) and sum(x x^T) on bf16 MFMA with fp32 accumulation;
 //   pddp_direction one workgroup per node: moments (summed partials, or
-//                  computed directly for small nodes) -> covariance -> power
-//                  iteration -> unit direction v with its largest-magnitude
-//                  component positive, and mu.v;
+//                  computed directly for small nodes) -> covariance ->
+//                  Lanczos -> top eigenvector v of the covariance with its
+//                  largest-magnitude component positive, and mu.v;
 //   pddp_project   p_i = x_i.v - mu.v for every query of the node (fp32);
 //   pddp_split     radix select of the rank-(C*floor(g/2)) projection and a
 //                  stable partition of the node's perm range.
@@ -36,7 +38,8 @@ namespace mcs {
 constexpr int PD_NT = 256;       // threads of the moment / direction / projection kernels
 constexpr int CHUNK_M = 2048;    // queries per partial-moment chunk
 constexpr int MSTEP = 64;        // queries staged in LDS per MFMA step
-constexpr int DEFAULT_ITERS = 32;
+constexpr int DEFAULT_STEPS = 32;  // Lanczos steps (Krylov dimension) by default
+constexpr int KRYLOV_MAX = 64;     // most Lanczos steps; the basis fills the moment staging LDS
 
 __device__ __forceinline__ int swz_st(int d) { return (d >> 1) & 7; }
 
@@ -180,11 +183,15 @@ __global__ __launch_bounds__(PD_NT) void pddp_moments(PddpParams p) {
 // live in registers in the MFMA accumulator layout of node_moments: wave w,
 // block b covers the 32x32 block (rb, cb) of sum(x x^T) with f = w*NBLK + b,
 // rb = f / (D/32), cb = f % (D/32), and lane (lq, hh) holds element e of it at
-// row rb*32 + 8*(e/4) + 4*hh + e%4, column cb*32 + lq.  The power iteration
-// runs on that layout: since the covariance is symmetric, y = C v is
+// row rb*32 + 8*(e/4) + 4*hh + e%4, column cb*32 + lq.  The Lanczos products
+// run on that layout: since the covariance is symmetric, y = C v is
 // y[c] = sum_r C[r][c] v[r], so every lane sums its 16 rows of one column,
 // the two half-waves are added with one lane swap, and the row blocks meet in
-// a small LDS array.  Two barriers per step; nothing D x D ever goes to LDS.
+// a small LDS array.  One barrier per step; nothing D x D ever goes to LDS.
+// The direction is the top eigenvector of the covariance (the node's
+// principal direction), found by Lanczos with full reorthogonalisation: the
+// top eigenpair of the small tridiagonal matrix (multisection on Sturm
+// counts, then inverse iteration, in fp64) gives the Ritz vector.
 // FROM_PARTS: the node's moments are summed from pddp_moments partials (large
 // nodes); otherwise the workgroup computes them itself.
 template <int D, bool FROM_PARTS>
@@ -195,8 +202,12 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   __shared__ MomentLds<D> L;
   __shared__ float sred[MSTEP / 4][D];
   __shared__ float part[2][RB][D];
-  __shared__ float mu[D], vec[D];
+  __shared__ float mu[D];
+  __shared__ float tri[2][KRYLOV_MAX];           // alpha, beta of the Lanczos recurrence
+  __shared__ double tri_d[KRYLOV_MAX], tri_x[KRYLOV_MAX];
   __shared__ int ish[2];
+  constexpr int NV = D / 64;                     // vector components per lane
+  static_assert(sizeof(MomentLds<D>) >= sizeof(float) * KRYLOV_MAX * D, "basis must fit the staging LDS");
   const int slot = blockIdx.x, bh = blockIdx.y;
   int off, n, g;
   if (!node_geom(p.N, p.C, p.level, slot, off, n, g)) return;
@@ -284,6 +295,9 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     if (lane == 0) ish[0] = bi;
   }
   __syncthreads();
+  // Lanczos basis vectors [KRYLOV_MAX][D] fp32, in the LDS of the moment
+  // staging buffers (idle from here on)
+  float* __restrict__ Vb = reinterpret_cast<float*>(&L);
   {
     const int best = ish[0];
 #pragma unroll
@@ -291,77 +305,241 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
       const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
       if (cb * 32 + lq == best) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) vec[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)] = acc[b][e];
+        for (int e = 0; e < 16; ++e) Vb[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)] = acc[b][e];
       }
     }
   }
   __syncthreads();
   // normalise the start column (wave 0; a zero column gives e_0)
   if (w == 0) {
-    float y[D / 64], s2 = 0.f;
+    float y[NV], s2 = 0.f;
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-      y[k] = vec[lane + 64 * k];
+    for (int k = 0; k < NV; ++k) {
+      y[k] = Vb[lane + 64 * k];
       s2 = fmaf(y[k], y[k], s2);
     }
+    s2 = wave_sum(s2);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const int c = lane + 64 * k;
-      vec[c] = s2 > 0.f ? y[k] * rsqrtf(s2) : (c == 0 ? 1.f : 0.f);
+      Vb[c] = s2 > 0.f ? y[k] * rsqrtf(s2) : (c == 0 ? 1.f : 0.f);
     }
   }
   __syncthreads();
-  // Power iteration, one barrier per step: every wave forms y = C v from the
-  // row-block partials (buffer it & 1), takes |y| itself, and writes the new v
-  // only for the rows its own blocks read (vec rows are private to a wave from
-  // here on; a zero y leaves v unchanged).
-  const int iters = p.iters > 0 ? p.iters : DEFAULT_ITERS;
+
+  // Lanczos with full reorthogonalisation.  Every wave runs the three-term
+  // recurrence on full-length vectors (lane holds components lane + 64*k),
+  // with bitwise the same arithmetic in the same order, so all waves hold the
+  // same alpha, beta and basis and leave the loop at the same step.  Only the
+  // product C v needs the workgroup: each wave multiplies its row block (the
+  // rows of v it reads are the ones it wrote itself), and the row-block
+  // partials meet in LDS, one barrier per step.  The new vector is made
+  // orthogonal to the whole basis by classical Gram-Schmidt, a second time
+  // when the first pass removed more than half of its squared norm.
+  const int steps = p.iters > 0 ? min(p.iters, KRYLOV_MAX) : DEFAULT_STEPS;
   const int myrb = (w * NBLK) / RB;       // row block of this wave's blocks
-  for (int it = 0; it < iters; ++it) {
-    const int pb = it & 1;
+  float vj[NV], vprev[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    vj[k] = Vb[lane + 64 * k];
+    vprev[k] = 0.f;
+  }
+  auto reorth = [&](int j, float (&wv)[NV]) {
+    float dw[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) dw[k] = 0.f;
+    int i = 0;
+    for (; i + 4 <= j + 1; i += 4) {
+      float vv[4][NV], h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        h[u] = 0.f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          vv[u][k] = Vb[(i + u) * D + lane + 64 * k];
+          h[u] = fmaf(vv[u][k], wv[k], h[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) h[u] = uniform_f(wave_sum(h[u]));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < NV; ++k) dw[k] = fmaf(h[u], vv[u][k], dw[k]);
+    }
+    for (; i <= j; ++i) {
+      float vv[NV], h = 0.f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        vv[k] = Vb[i * D + lane + 64 * k];
+        h = fmaf(vv[k], wv[k], h);
+      }
+      h = uniform_f(wave_sum(h));
+#pragma unroll
+      for (int k = 0; k < NV; ++k) dw[k] = fmaf(h, vv[k], dw[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) wv[k] -= dw[k];
+  };
+  auto sqnorm = [&](const float (&wv)[NV]) {
+    float s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) s2 = fmaf(wv[k], wv[k], s2);
+    return uniform_f(wave_sum(s2));
+  };
+  int m = 0;
+  float bprev = 0.f;
+  for (int j = 0; j < steps; ++j) {
+    const int pb = j & 1;
+    const float* __restrict__ vrow = Vb + j * D;
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
       float y = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) y = fmaf(acc[b][e], vec[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)], y);
+      for (int e = 0; e < 16; ++e) y = fmaf(acc[b][e], vrow[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)], y);
       y = halves_sum(y);
       if (hh == 0) part[pb][rb][cb * 32 + lq] = y;
     }
     __syncthreads();
-    float y[D / 64], s2 = 0.f;
+    float wv[NV], a = 0.f;
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
+    for (int k = 0; k < NV; ++k) {
       float v = 0.f;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) v += part[pb][rb][lane + 64 * k];
-      y[k] = v;
-      s2 = fmaf(v, v, s2);
+      wv[k] = v;
+      a = fmaf(vj[k], v, a);
     }
+    a = uniform_f(wave_sum(a));
+    if (w == 0 && lane == 0) tri[0][j] = a;
+    m = j + 1;
+    if (j + 1 >= steps) break;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
-    if (s2 > 0.f) {
-      const float inv = rsqrtf(s2);
+    for (int k = 0; k < NV; ++k) wv[k] = fmaf(-bprev, vprev[k], fmaf(-a, vj[k], wv[k]));
+    const float n0 = sqnorm(wv);
+    reorth(j, wv);
+    float n1 = sqnorm(wv);
+    bool invariant = !(n1 > 0.f);
+    if (!invariant && n1 <= 0.5f * n0) {
+      reorth(j, wv);
+      const float n2 = sqnorm(wv);
+      // a vector a second pass still shrinks by half lies in the basis up to
+      // rounding: the Krylov space is invariant and T already exact
+      invariant = !(n2 > 0.5f * n1);
+      n1 = n2;
+    }
+    if (invariant) break;
+    const float bnew = sqrtf(n1), inv = 1.f / bnew;
+    if (w == 0 && lane == 0) tri[1][j] = bnew;
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) {
-        const int c = lane + 64 * k;
-        if ((c >> 5) == myrb) vec[c] = y[k] * inv;
+    for (int k = 0; k < NV; ++k) {
+      vprev[k] = vj[k];
+      vj[k] = wv[k] * inv;
+      const int c = lane + 64 * k;
+      if ((c >> 5) == myrb) Vb[(j + 1) * D + c] = vj[k];
+    }
+    bprev = bnew;
+  }
+  // From here on only wave 0 works (no further barriers): the top eigenpair
+  // of the m x m tridiagonal T = tridiag(beta, alpha, beta), then the Ritz
+  // vector.  All of the basis is visible: its last vector was written before
+  // the last step's barrier.
+  if (w != 0) return;
+  double theta_hi;
+  {
+    // Gershgorin interval, then multisection on Sturm counts: lane l counts
+    // the eigenvalues below lo + (hi - lo) (l + 1) / 65, and the interval
+    // shrinks to the two shifts around the largest eigenvalue, 5 times.
+    double lo = INFINITY, hi = -INFINITY;
+    for (int i = 0; i < m; ++i) {
+      const double r = (i > 0 ? fabs((double)tri[1][i - 1]) : 0.0) + (i + 1 < m ? fabs((double)tri[1][i]) : 0.0);
+      lo = fmin(lo, (double)tri[0][i] - r);
+      hi = fmax(hi, (double)tri[0][i] + r);
+    }
+    if (m > 1 && hi > lo) {
+      for (int round = 0; round < 5; ++round) {
+        const double x = lo + (hi - lo) * (double)(lane + 1) / 65.0;
+        int cnt = 0;
+        double d = 1.0;
+        for (int i = 0; i < m; ++i) {
+          const double bb = i > 0 ? (double)tri[1][i - 1] : 0.0;
+          d = ((double)tri[0][i] - x) - (i > 0 ? bb * bb / d : 0.0);
+          if (d == 0.0) d = -1e-300;
+          cnt += d < 0.0;
+        }
+        const uint64_t above = __builtin_amdgcn_ballot_w64(cnt >= m);
+        if (above == 0) {
+          lo = lo + (hi - lo) * 64.0 / 65.0;
+        } else {
+          const int f = __builtin_ctzll(above);
+          const double nhi = lo + (hi - lo) * (double)(f + 1) / 65.0;
+          const double nlo = f > 0 ? lo + (hi - lo) * (double)f / 65.0 : lo;
+          lo = nlo;
+          hi = nhi;
+        }
       }
     }
+    theta_hi = hi + fmax(hi - lo, 1e-9 * fabs(hi)) + 1e-300;
   }
-  // each row block of vec now holds v (written by the wave that owns it)
-  __syncthreads();
+  // Inverse iteration with the shift sigma just above the largest eigenvalue:
+  // sigma I - T is positive definite there, so its LU recurrence needs no
+  // pivoting.  Two steps from the all-ones vector.  s goes through LDS.
+  if (m == 1) {
+    if (lane == 0) tri_x[0] = 1.0;
+  } else {
+    const double sigma = theta_hi;
+    for (int i = 0; i < m; ++i)
+      if (lane == 0) tri_x[i] = 1.0;
+    for (int iter = 0; iter < 2; ++iter) {
+      double d = 0.0, yprev = 0.0;
+      for (int i = 0; i < m; ++i) {        // forward: pivots d_i and y
+        const double bb = i > 0 ? (double)tri[1][i - 1] : 0.0;
+        const double dn = (sigma - (double)tri[0][i]) - (i > 0 ? bb * bb / d : 0.0);
+        const double yi = tri_x[i] + (i > 0 ? bb / d * yprev : 0.0);
+        d = dn;
+        yprev = yi;
+        if (lane == 0) {
+          tri_d[i] = dn;
+          tri_x[i] = yi;
+        }
+      }
+      double xnext = 0.0, s2 = 0.0;
+      for (int i = m - 1; i >= 0; --i) {   // back substitution
+        const double bb = i + 1 < m ? (double)tri[1][i] : 0.0;
+        const double xi = (tri_x[i] + bb * xnext) / tri_d[i];
+        xnext = xi;
+        s2 += xi * xi;
+        if (lane == 0) tri_x[i] = xi;
+      }
+      const double inv = 1.0 / sqrt(s2);
+      for (int i = 0; i < m; ++i)
+        if (lane == 0) tri_x[i] *= inv;
+    }
+  }
+  // Ritz vector y = sum_j s_j V_j, normalised
+  float y[NV], s2 = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) y[k] = 0.f;
+  for (int j = 0; j < m; ++j) {
+    const float sj = (float)tri_x[j];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) y[k] = fmaf(sj, Vb[j * D + lane + 64 * k], y[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < NV; ++k) s2 = fmaf(y[k], y[k], s2);
+  s2 = wave_sum(s2);
+  const float yinv = s2 > 0.f ? rsqrtf(s2) : 0.f;
   // sign: largest-magnitude component positive (first on ties); mu.v
-  if (w == 0) {
+  {
     float bv = -1.f, mv = 0.f;
     int bi = 0;
     float sgnv = 0.f;
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
+    for (int k = 0; k < NV; ++k) {
       const int c = lane + 64 * k;
-      const float x = vec[c];
+      const float x = y[k] * yinv;
+      y[k] = x;
       if (fabsf(x) > bv) {
         bv = fabsf(x);
         bi = c;
@@ -384,7 +562,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     const float sgn = sgnv < 0.f ? -1.f : 1.f;
     float* __restrict__ out = p.dir + ((size_t)bh * p.nodes + slot) * (D + 4);
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) out[lane + 64 * k] = sgn * vec[lane + 64 * k];
+    for (int k = 0; k < NV; ++k) out[lane + 64 * k] = sgn * y[k];
     if (lane == 0) out[D] = sgn * mv;
   }
 }

@@ -7,9 +7,10 @@
 
 namespace mcs {
 
-__global__ __launch_bounds__(256) void residual_kernel(const uint16_t* __restrict__ od,
-                                                       const uint16_t* __restrict__ osp,
-                                                       uint16_t* __restrict__ r, int64_t n) {
+// r may alias od or osp: every element is read and then written by the same
+// thread, and no thread touches another's elements.
+__global__ __launch_bounds__(256) void residual_kernel(const uint16_t* od, const uint16_t* osp,
+                                                       uint16_t* r, int64_t n) {
   const int64_t nvec = n / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
