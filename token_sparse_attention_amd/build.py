@@ -28,6 +28,13 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  pddp.hip: MFMA accumulators in VGPRs (the
+# direction kernel copies the node's moments into VGPRs for its VALU
+# matrix-vector products anyway; with AGPR accumulators the unused copies
+# count against occupancy).
+EXTRA_FLAGS = {"pddp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -53,7 +60,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     compile_flags = [f for f in FLAGS if f != "-shared"]
     objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in sources]
-    cmds = [[hipcc(), *compile_flags, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    cmds = [[hipcc(), *compile_flags, *EXTRA_FLAGS.get(os.path.basename(src), []),
+             "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
             for src, obj in zip(sources, objs)]
     with ThreadPoolExecutor(max(1, min(len(cmds), os.cpu_count() or 1, 8))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

@@ -83,10 +83,19 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the 64 lanes of a wave.  Every step pairs each lane with a partner
-// under a permutation that is its own inverse (xor 1, xor 2, mirror within 8
-// and within 16 lanes, xor 16, xor 32), so both lanes of a pair add the same
-// two values and every lane ends with bitwise the same total.
+// Values of lanes L and L^16 combined, as halves_sum: v_permlane16_swap
+// exchanges the odd 16-lane rows of one operand with the even rows of the
+// other, so with both operands x every lane receives (own, partner).
+__device__ __forceinline__ float rows_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the 64 lanes of a wave, all on the VALU.  Every step pairs each
+// lane with a partner under a permutation that is its own inverse (xor 1,
+// xor 2, mirror within 8 and within 16 lanes, xor 16, xor 32), so both lanes
+// of a pair add the same two values and every lane ends with bitwise the
+// same total.
 __device__ __forceinline__ float wave_sum(float x) {
   auto dpp = [](float v, auto ctrl_c) {
     constexpr int CTRL = decltype(ctrl_c)::value;
@@ -96,8 +105,45 @@ __device__ __forceinline__ float wave_sum(float x) {
   x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
   x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
   x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
-  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));   // lane ^ 16
-  return halves_sum(x);
+  return halves_sum(rows_sum(x));
+}
+
+// Eight sums over the 64 lanes of a wave at once, by recursive halving: at
+// each exchange a lane keeps half of its values, each added to its partner's
+// copy.  v_permlane32_swap(x, y) swaps lanes 32..63 of x with lanes 0..31 of
+// y, so a lower lane receives (own x, partner x) and an upper lane
+// (partner y, own y); v_permlane16_swap does the same between the odd and
+// even 16-lane rows; a DPP mirror pairs the two 8-lane halves of a row.
+// Value k ends up fully summed in lanes 8k..8k+7 and is read from lane 8k,
+// so every wave that runs this on the same inputs gets bitwise the same
+// sums.  The sums are returned in h (wave-uniform).
+__device__ __forceinline__ void wave_sum8(float (&h)[8]) {
+  const int lane = __lane_id();
+  float a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {      // lanes l, l^32: lower keeps 0..3, upper 4..7
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(h[i]), __float_as_uint(h[i + 4]), false,
+                                              false);
+    a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {      // lanes l, l^16: even rows keep a0, a1, odd rows a2, a3
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + 2]), false,
+                                              false);
+    b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  auto dpp = [](float v, auto ctrl_c) {
+    constexpr int CTRL = decltype(ctrl_c)::value;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+  };
+  const bool upper8 = (lane & 8) != 0;   // lanes l, 15-l of a row: low half keeps b0, high b1
+  const float send = upper8 ? b[0] : b[1];
+  float c = (upper8 ? b[1] : b[0]) + dpp(send, std::integral_constant<int, 0x140>{});   // row_mirror
+  c += dpp(c, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  c += dpp(c, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  c += dpp(c, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 8 * k));
 }
 
 // A value that is the same in every lane, moved to a scalar register.

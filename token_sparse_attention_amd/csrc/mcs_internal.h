@@ -44,21 +44,39 @@ GroupPlan plan_group(int BH, int N, int D, int C);
 hipError_t run_group(const uint16_t* q, int32_t* perm, int BH, int N, int D, int C, int iters,
                      void* ws, const GroupPlan& plan, hipStream_t s);
 
-// Node geometry of the median-split tree: the node reached from the root by
-// the top `level` bits of `slot` (most significant first, 0 = left).  Returns
-// false when that node does not exist or is a leaf (<= one group).
-__host__ __device__ inline bool node_geom(int N, int C, int level, int slot, int& off, int& n,
-                                          int& g) {
+// Shape of the median-split tree.  A node of g > 1 groups has a left child of
+// floor(g/2) groups (C*floor(g/2) queries) and a right child of the rest.
+// Repeated halving leaves, d levels below a node of g groups, nodes of
+// floor(g/2^d) or floor(g/2^d) + 1 groups, (g mod 2^d) of the latter; so the
+// number of split nodes (> 1 group) there is closed-form.
+__host__ __device__ inline int split_nodes_below(int g, int d) {
+  const int q = g >> d, r = g & ((1 << d) - 1);
+  return q >= 2 ? (1 << d) : (q == 1 ? r : 0);
+}
+
+// Number of split nodes at tree level `level` of a head of N queries.
+__host__ __device__ inline int split_nodes_at(int N, int C, int level) {
+  return split_nodes_below((N + C - 1) / C, level);
+}
+
+// The rank-th split node (left to right) at `level`: its offset in the head's
+// perm row, its size n and group count g (> 1).  Returns false if rank is out
+// of range.  Kernels launch one workgroup per split node, so consecutive
+// workgroups (which the hardware deals to consecutive XCDs) always have work.
+__host__ __device__ inline bool node_by_rank(int N, int C, int level, int rank, int& off, int& n,
+                                             int& g) {
   off = 0;
   n = N;
   g = (N + C - 1) / C;
+  if (rank < 0 || rank >= split_nodes_below(g, level)) return false;
   for (int i = 0; i < level; ++i) {
-    if (g <= 1) return false;
     const int half = g / 2, nl = C * half;
-    if (((slot >> (level - 1 - i)) & 1) == 0) {
+    const int left = split_nodes_below(half, level - 1 - i);
+    if (rank < left) {
       n = nl;
       g = half;
     } else {
+      rank -= left;
       off += nl;
       n -= nl;
       g -= half;

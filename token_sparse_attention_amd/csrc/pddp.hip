@@ -12,9 +12,10 @@
 //
 // Tree shape.  A node of n queries forms g = ceil(n/C) groups; a node with
 // g > 1 sends the first C*floor(g/2) queries (in projection order) left and the
-// rest right.  The shape depends only on (N, C), so every kernel finds its node
-// from (level, slot) by walking the split sizes down from the root
-// (node_geom), and every node owns the contiguous range [off, off+n) of its
+// rest right.  The shape depends only on (N, C), so the kernels of a level are
+// launched over the level's split nodes only, and each workgroup finds its
+// node from its rank by walking the split sizes down from the root
+// (node_by_rank); every node owns the contiguous range [off, off+n) of its
 // head's perm row.  perm starts as the identity and every split is a stable
 // partition, so inside every node the queries stay in ascending id order and a
 // tie in projection is broken by query id simply by position.
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_moments(PddpParams p) {
   __shared__ float sred[PD_NT / (D / 8)][D];
   const int c = blockIdx.x, slot = blockIdx.y, bh = blockIdx.z;
   int off, n, g;
-  if (!node_geom(p.N, p.C, p.level, slot, off, n, g)) return;
+  if (!node_by_rank(p.N, p.C, p.level, slot, off, n, g)) return;
   const int m0 = c * CHUNK_M;
   if (m0 >= n) return;
   const int m1 = min(n, m0 + CHUNK_M);
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   static_assert(sizeof(MomentLds<D>) >= sizeof(float) * KRYLOV_MAX * D, "basis must fit the staging LDS");
   const int slot = blockIdx.x, bh = blockIdx.y;
   int off, n, g;
-  if (!node_geom(p.N, p.C, p.level, slot, off, n, g)) return;
+  if (!node_by_rank(p.N, p.C, p.level, slot, off, n, g)) return;
   const size_t head = (size_t)bh * p.N;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
 
@@ -344,15 +345,26 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     vj[k] = Vb[lane + 64 * k];
     vprev[k] = 0.f;
   }
-  auto reorth = [&](int j, float (&wv)[NV]) {
+  // One classical Gram-Schmidt pass against V[0..j]: h_i = V_i.w for all i
+  // from the same w, then w -= sum h_i V_i.  The squared norm of w before the
+  // pass is reduced in the same batch; the norm after it follows from
+  // Pythagoras (V orthonormal), |w'|^2 = |w|^2 - sum h_i^2, returned in *after.
+  auto reorth = [&](int j, float (&wv)[NV], float& before, float& after) {
     float dw[NV];
+    float s2 = 0.f;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) dw[k] = 0.f;
+    for (int k = 0; k < NV; ++k) {
+      dw[k] = 0.f;
+      s2 = fmaf(wv[k], wv[k], s2);
+    }
+    before = 0.f;
+    float hsq = 0.f;
     int i = 0;
-    for (; i + 4 <= j + 1; i += 4) {
-      float vv[4][NV], h[4];
+    bool first = true;
+    for (; i + 8 <= j + 1; i += 8) {
+      float vv[8][NV], h[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         h[u] = 0.f;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
@@ -360,46 +372,72 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
           h[u] = fmaf(vv[u][k], wv[k], h[u]);
         }
       }
+      if (first) before = uniform_f(wave_sum(s2));
+      first = false;
+      wave_sum8(h);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) h[u] = uniform_f(wave_sum(h[u]));
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u) {
+        hsq = fmaf(h[u], h[u], hsq);
 #pragma unroll
         for (int k = 0; k < NV; ++k) dw[k] = fmaf(h[u], vv[u][k], dw[k]);
-    }
-    for (; i <= j; ++i) {
-      float vv[NV], h = 0.f;
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        vv[k] = Vb[i * D + lane + 64 * k];
-        h = fmaf(vv[k], wv[k], h);
       }
-      h = uniform_f(wave_sum(h));
+    }
+    if (i <= j) {
+      float vv[8][NV], h[8];
 #pragma unroll
-      for (int k = 0; k < NV; ++k) dw[k] = fmaf(h, vv[k], dw[k]);
+      for (int u = 0; u < 8; ++u) {
+        h[u] = 0.f;
+        if (i + u <= j) {
+#pragma unroll
+          for (int k = 0; k < NV; ++k) {
+            vv[u][k] = Vb[(i + u) * D + lane + 64 * k];
+            h[u] = fmaf(vv[u][k], wv[k], h[u]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < NV; ++k) vv[u][k] = 0.f;
+        }
+      }
+      if (first) before = uniform_f(wave_sum(s2));
+      wave_sum8(h);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        hsq = fmaf(h[u], h[u], hsq);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) dw[k] = fmaf(h[u], vv[u][k], dw[k]);
+      }
     }
 #pragma unroll
     for (int k = 0; k < NV; ++k) wv[k] -= dw[k];
-  };
-  auto sqnorm = [&](const float (&wv)[NV]) {
-    float s2 = 0.f;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) s2 = fmaf(wv[k], wv[k], s2);
-    return uniform_f(wave_sum(s2));
+    after = before - hsq;
   };
   int m = 0;
   float bprev = 0.f;
   for (int j = 0; j < steps; ++j) {
     const int pb = j & 1;
     const float* __restrict__ vrow = Vb + j * D;
+    {
+      // the row block is the same for all of this wave's blocks, so the 16
+      // entries of v are loaded once; two chains per block, all interleaved
+      const int rb0 = (w * NBLK) / RB;
+      float vr[16], ya[NBLK], yb[NBLK];
 #pragma unroll
-    for (int b = 0; b < NBLK; ++b) {
-      const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
-      float y = 0.f;
+      for (int e = 0; e < 16; ++e) vr[e] = vrow[rb0 * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) y = fmaf(acc[b][e], vrow[rb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)], y);
-      y = halves_sum(y);
-      if (hh == 0) part[pb][rb][cb * 32 + lq] = y;
+      for (int b = 0; b < NBLK; ++b) ya[b] = yb[b] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2)
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) {
+          ya[b] = fmaf(acc[b][e], vr[e], ya[b]);
+          yb[b] = fmaf(acc[b][e + 1], vr[e + 1], yb[b]);
+        }
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int f = w * NBLK + b, rb = f / RB, cb = f % RB;
+        const float y = halves_sum(ya[b] + yb[b]);
+        if (hh == 0) part[pb][rb][cb * 32 + lq] = y;
+      }
     }
     __syncthreads();
     float wv[NV], a = 0.f;
@@ -417,18 +455,21 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     if (j + 1 >= steps) break;
 #pragma unroll
     for (int k = 0; k < NV; ++k) wv[k] = fmaf(-bprev, vprev[k], fmaf(-a, vj[k], wv[k]));
-    const float n0 = sqnorm(wv);
-    reorth(j, wv);
-    float n1 = sqnorm(wv);
-    bool invariant = !(n1 > 0.f);
+    float n0, n1;
+    reorth(j, wv, n0, n1);
+    bool invariant = !(n0 > 0.f);
     if (!invariant && n1 <= 0.5f * n0) {
-      reorth(j, wv);
-      const float n2 = sqnorm(wv);
+      // the pass removed more than half of the vector: the Pythagorean norm
+      // is unreliable, and the vector is cleaned a second time
+      float m1, m2;
+      reorth(j, wv, m1, m2);
       // a vector a second pass still shrinks by half lies in the basis up to
       // rounding: the Krylov space is invariant and T already exact
-      invariant = !(n2 > 0.5f * n1);
-      n1 = n2;
+      invariant = !(m1 > 0.f) || m2 <= 0.5f * m1;
+      n1 = m2;
     }
+    // the last pass removed less than half of the squared norm, so its
+    // Pythagorean norm is accurate to a few ulps
     if (invariant) break;
     const float bnew = sqrtf(n1), inv = 1.f / bnew;
     if (w == 0 && lane == 0) tri[1][j] = bnew;
@@ -573,7 +614,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_project(PddpParams p) {
   constexpr int RPP = PD_NT / CH;   // queries per pass
   const int c = blockIdx.x, slot = blockIdx.y, bh = blockIdx.z;
   int off, n, g;
-  if (!node_geom(p.N, p.C, p.level, slot, off, n, g)) return;
+  if (!node_by_rank(p.N, p.C, p.level, slot, off, n, g)) return;
   const int span = p.cpn > 1 ? CHUNK_M : n;
   const int m0 = c * span;
   if (m0 >= n) return;
@@ -626,7 +667,7 @@ __global__ __launch_bounds__(NT) void pddp_split(PddpParams p) {
   __shared__ RadixLds<NT> L;
   const int slot = blockIdx.x, bh = blockIdx.y;
   int off, n, g;
-  if (!node_geom(p.N, p.C, p.level, slot, off, n, g)) return;
+  if (!node_by_rank(p.N, p.C, p.level, slot, off, n, g)) return;
   const int r = p.C * (g / 2);
   const size_t head = (size_t)bh * p.N;
   const float* __restrict__ pr = p.proj + head + off;
@@ -649,6 +690,22 @@ __global__ void pddp_init(int32_t* perm, int N, int64_t total) {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Largest node (queries) at a level.  Only the rightmost node can be short
+// (it holds the remainder group), and it is a split node whenever the level
+// has any; every other node holds C * (its groups) queries, q or q + 1 groups
+// with q = G >> level, and q + 1 occurs off the rightmost node when at least
+// two nodes have it (G mod 2^level >= 2).
+static int level_max_n(int N, int C, int lv) {
+  const int G = (N + C - 1) / C;
+  const int cnt = split_nodes_below(G, lv);
+  if (cnt == 0) return 0;
+  int off, n, g;
+  node_by_rank(N, C, lv, cnt - 1, off, n, g);
+  const int q = G >> lv, r = G & ((1 << lv) - 1);
+  if (cnt >= 2) n = max(n, C * (r >= 2 ? q + 1 : q));
+  return n;
+}
+
 GroupPlan plan_group(int BH, int N, int D, int C) {
   GroupPlan pl;
   const int G = (N + C - 1) / C;
@@ -656,15 +713,12 @@ GroupPlan plan_group(int BH, int N, int D, int C) {
   while ((1 << L) < G) ++L;
   pl.levels = L;
   pl.max_slots = 0;
-  pl.max_nodes = L > 0 ? (1 << (L - 1)) : 1;
+  pl.max_nodes = 1;
   for (int lv = 0; lv < L; ++lv) {
-    int maxn = 0;
-    for (int s = 0; s < (1 << lv); ++s) {
-      int off, n, g;
-      if (node_geom(N, C, lv, s, off, n, g) && n > maxn) maxn = n;
-    }
-    const int cpn = (maxn + CHUNK_M - 1) / CHUNK_M;
-    if (cpn > 1 && (1 << lv) * cpn > pl.max_slots) pl.max_slots = (1 << lv) * cpn;
+    const int nodes = split_nodes_at(N, C, lv);
+    if (nodes > pl.max_nodes) pl.max_nodes = nodes;
+    const int cpn = (level_max_n(N, C, lv) + CHUNK_M - 1) / CHUNK_M;
+    if (cpn > 1 && nodes * cpn > pl.max_slots) pl.max_slots = nodes * cpn;
   }
   size_t o = 0;
   pl.proj_off = o;
@@ -682,14 +736,11 @@ GroupPlan plan_group(int BH, int N, int D, int C) {
 template <int D>
 static hipError_t group_levels(PddpParams p, int BH, const GroupPlan& pl, hipStream_t s) {
   for (int lv = 0; lv < pl.levels; ++lv) {
-    int maxn = 0;
-    for (int sl = 0; sl < (1 << lv); ++sl) {
-      int off, n, g;
-      if (node_geom(p.N, p.C, lv, sl, off, n, g) && n > maxn) maxn = n;
-    }
+    const int maxn = level_max_n(p.N, p.C, lv);
+    const int nodes = split_nodes_at(p.N, p.C, lv);
+    if (nodes == 0) continue;
     p.level = lv;
     p.cpn = (maxn + CHUNK_M - 1) / CHUNK_M;
-    const int nodes = 1 << lv;
     if (p.cpn > 1) {
       hipLaunchKernelGGL(pddp_moments<D>, dim3(p.cpn, nodes, BH), dim3(PD_NT), 0, s, p);
     }
