@@ -190,3 +190,21 @@ def test_power_iteration_closed_form_after_t_steps(steps):
     want /= np.linalg.norm(want)
     np.testing.assert_allclose(mu, 0.0, atol=1e-15)
     np.testing.assert_allclose(vec, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("steps", [1, 5, 20])
+def test_power_iteration_closed_form_unequal_diagonal(steps):
+    # points +-sqrt(2) u1, +-sqrt(1.8) u2 with u1 = (cos 30, sin 30), u2 =
+    # (-sin 30, cos 30): covariance u1 u1^T + 0.9 u2 u2^T, diagonal (0.975,
+    # 0.925), so the start is column 0 = C e0 = cos30 u1 - 0.9 sin30 u2 and t
+    # steps give a direction proportional to u1 - 0.9^(t+1) tan30 u2 (the
+    # other column would give u1 + 0.9^(t+1) cot30 u2)
+    th = np.pi / 6
+    u1 = np.array([np.cos(th), np.sin(th)])
+    u2 = np.array([-np.sin(th), np.cos(th)])
+    pts = np.stack([np.sqrt(2) * u1, -np.sqrt(2) * u1, np.sqrt(1.8) * u2, -np.sqrt(1.8) * u2])
+    _, vec = oracle.principal_direction(pts, mode="power", power_iters=steps)
+    want = u1 - 0.9 ** (steps + 1) * np.tan(th) * u2
+    want /= np.linalg.norm(want)
+    want = want if want[np.argmax(np.abs(want))] > 0 else -want
+    np.testing.assert_allclose(vec, want, rtol=0, atol=1e-12)
