@@ -216,6 +216,25 @@ MCS_API mcs_status mcs_group(const uint16_t* q, int32_t* perm, mcs_dims d, int32
  * directions, and partial moments of the large nodes near the root). */
 MCS_API size_t mcs_group_workspace(mcs_dims d, int32_t C);
 
+/*
+ * mcs_group for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * grouping and results as mcs_group, with no workspace argument: the scratch
+ * is a static device array of 64 MiB that the library holds on every device
+ * its code is loaded on, until the process ends.  Heads are processed in
+ * chunks whose workspace fits it (4.7 MiB per head at N = 75600, D = 128,
+ * C = 128); a call whose single head needs more than 64 MiB of workspace
+ * (mcs_group_workspace with B = H = 1) returns MCS_E_WORKSPACE and enqueues
+ * nothing.  Runs on the calling thread's current device, whose stream must be
+ * passed.  Every call on a device shares that device's scratch, which keeps
+ * the last call's contents: calls on one stream are ordered and safe, but
+ * calls that overlap in time on one device (other streams, other threads)
+ * race and give wrong results.  The first call on a device looks up the
+ * scratch's address (hipGetSymbolAddress); no call allocates or frees.
+ */
+MCS_API mcs_status mcs_group_noalloc(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C,
+                             int32_t lanczos_steps, void* stream);
+
 /* Static description of a status code. */
 MCS_API const char* mcs_status_string(mcs_status s);
 

@@ -47,6 +47,7 @@ def lib():
     lib.mcs_select_two_pass.argtypes = [P, P, P, P, P, Dims, I32, I32, F, P, SZ, P]
     lib.mcs_topk.argtypes = [P, P, I64, I32, I32, P]
     lib.mcs_group.argtypes = [P, P, Dims, I32, I32, P, SZ, P]
+    lib.mcs_group_noalloc.argtypes = [P, P, Dims, I32, I32, P]
     lib.mcs_group_workspace.argtypes = [Dims, I32]
     lib.mcs_group_workspace.restype = SZ
     lib.mcs_select_workspace.argtypes = [Dims, I32, I32]
@@ -60,7 +61,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -146,6 +147,23 @@ def test_select_group_topk_residual_validation(lib):
     assert lib.mcs_topk(None, B_, 3, 10, 5, None) == c["MCS_E_NULL"]
     assert lib.mcs_residual_update(A, B_, C_, 0, None) == c["MCS_E_SHAPE"]
     assert lib.mcs_residual_update(A, B_ + 8, C_, 10, None) == c["MCS_E_ALIGN"]
+
+
+def test_group_noalloc_validation(lib):
+    # every check runs on the host before the scratch is looked up, so none
+    # of these needs a device
+    c = _codes()
+    d = Dims(1, 2, 1000, 128)
+    assert lib.mcs_group_noalloc(None, B_, d, 128, 0, None) == c["MCS_E_NULL"]
+    assert lib.mcs_group_noalloc(A + 4, B_, d, 128, 0, None) == c["MCS_E_ALIGN"]
+    assert lib.mcs_group_noalloc(A, B_, Dims(1, 2, 1000, 96), 128, 0, None) == c["MCS_E_HEAD_DIM"]
+    assert lib.mcs_group_noalloc(A, B_, d, 100, 0, None) == c["MCS_E_GROUP_SIZE"]
+    assert lib.mcs_group_noalloc(A, B_, d, 128, 65, None) == c["MCS_E_ARG"]
+    # one head of N = 8388607, D = 128 needs more workspace than the 64 MiB scratch
+    big = Dims(1, 1, 8388607, 128)
+    assert lib.mcs_group_workspace(big, 128) > 64 << 20
+    assert lib.mcs_group_noalloc(A, B_, big, 128, 0, None) == c["MCS_E_WORKSPACE"]
+    assert b"scratch" in lib.mcs_last_error()
 
 
 def test_group_workspace_grows_with_partials(lib):

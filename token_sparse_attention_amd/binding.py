@@ -50,6 +50,7 @@ _SIGS = {
     "mcs_topk": ([_P, _P, _I64, _I32, _I32, _P], _I32),
     "mcs_group": ([_P, _P, Dims, _I32, _I32, _P, _SZ, _P], _I32),
     "mcs_group_workspace": ([Dims, _I32], _SZ),
+    "mcs_group_noalloc": ([_P, _P, Dims, _I32, _I32, _P], _I32),
     "mcs_status_string": ([_I32], ctypes.c_char_p),
     "mcs_last_error": ([], ctypes.c_char_p),
     "mcs_version": ([], _I32),
@@ -266,6 +267,16 @@ def group(q, C, lanczos_steps=0, out=None, workspace=None):
         _like(workspace, "workspace", torch.uint8, (workspace.numel(),), q.device)
     _check(_lib.mcs_group(_ptr(q), _ptr(out), dims_of(q), C, lanczos_steps, _ptr(workspace),
                           workspace.numel(), _stream(q)))
+    return out
+
+
+def group_noalloc(q, C, lanczos_steps=0, out=None):
+    """mcs_group_noalloc: mcs_group with the library's static scratch (no workspace)."""
+    _need(q, "q", torch.bfloat16, 4)
+    B, H, N, D = q.shape
+    out = torch.empty((B, H, N), dtype=torch.int32, device=q.device) if out is None else out
+    _like(out, "out", torch.int32, (B, H, N), q.device)
+    _check(_lib.mcs_group_noalloc(_ptr(q), _ptr(out), dims_of(q), C, lanczos_steps, _stream(q)))
     return out
 
 

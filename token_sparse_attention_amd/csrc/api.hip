@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mcs.h"
 #include "mcs_internal.h"
 
@@ -80,6 +82,39 @@ mcs_status launched(const char* fn, hipError_t e) {
 size_t select_ws_per_head(mcs_dims d, int32_t C) {
   const size_t G = ((size_t)d.N + C - 1) / C;
   return G * (size_t)d.N * sizeof(float);
+}
+
+}  // namespace
+
+// Scratch of mcs_group_noalloc: a static device array, so that call needs no
+// allocation.  Each device the library's code is loaded on holds its own
+// copy until the process ends.  Host code never uses the symbol itself (its
+// host-side name is a stand-in, not a device address): the device address
+// comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kGroupScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kGroupScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the calling thread's current device.
+hipError_t group_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -258,6 +293,37 @@ mcs_status mcs_group(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C, in
   if (!aligned16(ws)) return fail(MCS_E_ALIGN, "%s: ws is not 16-byte aligned", fn);
   return launched(fn, mcs::run_group(q, perm, d.B * d.H, d.N, d.D, C, lanczos_steps, ws, plan,
                                      (hipStream_t)stream));
+}
+
+mcs_status mcs_group_noalloc(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C,
+                             int32_t lanczos_steps, void* stream) {
+  const char* fn = "mcs_group_noalloc";
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(perm);
+  mcs_status st;
+  if ((st = check_dims(fn, d)) != MCS_OK) return st;
+  if ((st = check_group_size(fn, C)) != MCS_OK) return st;
+  if (lanczos_steps > 64)
+    return fail(MCS_E_ARG, "%s: lanczos_steps must be <= 64 (got %d)", fn, lanczos_steps);
+  const int BH = d.B * d.H;
+  const size_t one = mcs::plan_group(1, d.N, d.D, C).bytes;
+  if (one > kGroupScratchBytes)
+    return fail(MCS_E_WORKSPACE, "%s: one head needs %zu bytes of scratch, more than the %zu the library holds",
+                fn, one, kGroupScratchBytes);
+  // heads per launch sequence: as many as the scratch holds
+  int nh = (int)((size_t)BH < kGroupScratchBytes / one ? (size_t)BH : kGroupScratchBytes / one);
+  while (nh > 1 && mcs::plan_group(nh, d.N, d.D, C).bytes > kGroupScratchBytes) --nh;
+  void* ws = nullptr;
+  hipError_t e = group_scratch(&ws);
+  if (e != hipSuccess) return launched(fn, e);
+  for (int bh0 = 0; bh0 < BH; bh0 += nh) {
+    const int n = BH - bh0 < nh ? BH - bh0 : nh;
+    const mcs::GroupPlan plan = mcs::plan_group(n, d.N, d.D, C);
+    e = mcs::run_group(q + (size_t)bh0 * d.N * d.D, perm + (size_t)bh0 * d.N, n, d.N, d.D, C,
+                       lanczos_steps, ws, plan, (hipStream_t)stream);
+    if (e != hipSuccess) return launched(fn, e);
+  }
+  return ok();
 }
 
 const char* mcs_status_string(mcs_status s) {
