@@ -131,6 +131,25 @@ MCS_API mcs_status mcs_sparse_attn_f32out(const uint16_t* q, const uint16_t* k, 
                                   int32_t K, float scale, void* stream);
 
 /*
+ * mcs_sparse_attn with two extensions, for the selection diagnostics and the
+ * block-sparse comparison below:
+ *   kv_count: int32 [B,H,G] or NULL.  Group g attends to its first
+ *             kv_count[b,h,g] ids only (a value outside [1, K] is clamped
+ *             into it); the id lists stay K apart in kv_idx.  NULL: K each.
+ *   lse:      float32 [B,H,N] or NULL: ln sum_{j selected} exp(scale q_i.k_j),
+ *             the log-sum-exp over each query's selected keys (with the dense
+ *             LSE of mcs_dense_attn, exp(lse - lse_dense) is the dense
+ *             attention mass the selection keeps).  lse and residual cannot
+ *             both be given.
+ *   o:        float32 when o_f32 != 0, else bf16 [B,H,N,D].
+ * Other arguments, layouts and checks as mcs_sparse_attn.
+ */
+MCS_API mcs_status mcs_sparse_attn_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* perm, const int32_t* kv_idx, const int32_t* kv_count,
+                              const uint16_t* residual, void* o, int32_t o_f32, float* lse,
+                              mcs_dims d, int32_t C, int32_t K, float scale, void* stream);
+
+/*
  * Anchor-step residual (wispaper.ai, "Residual correction recovers the
  * discarded tail": at an anchor the method records dense minus sparse output).
  *   residual[e] = bf16(float(o_dense[e]) - float(o_sparse[e])),  e < n_elems
@@ -234,6 +253,48 @@ MCS_API size_t mcs_group_workspace(mcs_dims d, int32_t C);
  */
 MCS_API mcs_status mcs_group_noalloc(const uint16_t* q, int32_t* perm, mcs_dims d, int32_t C,
                              int32_t lanczos_steps, void* stream);
+
+/*
+ * Mean-pooled block selection, the selector of standard block-sparse
+ * attention that the pages compare against (wispaper.ai, "Mean-pooled block
+ * scoring misses high-mass tokens"; agihunt.info, the kernel comparison).
+ * Keys form blocks of 64 consecutive tokens (the last one may be short).  For
+ * each query group g (perm[g*C ..], as in mcs_select) the score of key block
+ * b is scale * mean_{i in g}(q_i) . mean_{j in b}(k_j) (fp32); the K/64
+ * blocks of largest score are kept, equal scores going to the smaller block
+ * id.  Out: kv_idx int32 [B,H,G,K], the token ids of the kept blocks in
+ * ascending order, and kv_count int32 [B,H,G], the number of real token ids
+ * (K, less the missing tail when the short last block is kept; the slots past
+ * it repeat id N-1).  The pair feeds mcs_sparse_attn_ex.
+ * K: a multiple of 64 with 64 <= K <= 64 * ceil(N/64); ceil(N/64) <= 4096.
+ * ws: device workspace of mcs_select_blocks_workspace(d) bytes (block means).
+ */
+MCS_API mcs_status mcs_select_blocks(const uint16_t* q, const uint16_t* k, const int32_t* perm,
+                             int32_t* kv_idx, int32_t* kv_count, mcs_dims d, int32_t C,
+                             int32_t K, float scale, void* ws, size_t ws_bytes, void* stream);
+MCS_API size_t mcs_select_blocks_workspace(mcs_dims d);
+
+/*
+ * Per-query quality of a selection (ai.info, "Main Findings" and
+ * "Methodology in Plain English": attention recall and the relative L1
+ * error of the renormalised sparse output).  For every query row r of
+ * [B,H,N]:
+ *   recall[r] = exp(lse_sparse[r] - lse_dense[r])      (kept dense mass)
+ *   l1[r]     = sum_c |o_sparse[r,c] - o_dense[r,c]|
+ *   l1_ref[r] = sum_c |o_dense[r,c]|
+ * In: lse_dense (mcs_dense_attn), lse_sparse (mcs_sparse_attn_ex, no
+ * residual) float32 [B,H,N]; o_dense, o_sparse float32 [B,H,N,D].  Out:
+ * recall, l1, l1_ref float32 [B,H,N].  The relative L1 error is
+ * sum(l1) / sum(l1_ref) (mcs_row_sums).
+ */
+MCS_API mcs_status mcs_query_quality(const float* lse_dense, const float* lse_sparse,
+                             const float* o_dense, const float* o_sparse, float* recall,
+                             float* l1, float* l1_ref, mcs_dims d, void* stream);
+
+/* out[r] = sum_i x[r*n + i] in fp64, summed in a fixed order (deterministic).
+ * In: x float32 [rows, n].  Out: out float64 [rows].  1 <= rows < 2^31. */
+MCS_API mcs_status mcs_row_sums(const float* x, double* out, int64_t rows, int64_t n,
+                        void* stream);
 
 /* Static description of a status code. */
 MCS_API const char* mcs_status_string(mcs_status s);

@@ -84,6 +84,26 @@ def block_sums(x: np.ndarray, N: int) -> np.ndarray:
     return pad.reshape(nb, KV_BLOCK).sum(axis=1)
 
 
+def block_means(k) -> np.ndarray:
+    """Mean key of every KV block (D1: KV_BLOCK consecutive keys, last one short)."""
+    k = _f64(k)
+    N = k.shape[0]
+    return np.stack([k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].mean(axis=0) for b in range(-(-N // KV_BLOCK))])
+
+
+def mean_pooled_scores(q, kbar, rows, scale: float) -> np.ndarray:
+    """D5: score of every KV block for the query block `rows`:
+    scale * mean(q_rows) . mean(k_block)."""
+    return scale * (kbar @ _f64(q)[rows].mean(axis=0))
+
+
+def mean_pooled_blocks(q, kbar, rows, K: int, scale: float) -> np.ndarray:
+    """The KV blocks mean-pooled block selection keeps for the query block
+    `rows` at budget K (max(1, K // KV_BLOCK) blocks, D3, ties to the smaller
+    block id), ascending."""
+    return _top_ids(mean_pooled_scores(q, kbar, rows, scale), max(1, K // KV_BLOCK))
+
+
 def diagnose_groups(q, k, v, groups: Sequence[np.ndarray], Ks: Sequence[int], scale: float) -> dict:
     """Recall and output error of the four selectors for one head.
 
@@ -102,15 +122,14 @@ def diagnose_groups(q, k, v, groups: Sequence[np.ndarray], Ks: Sequence[int], sc
     o_dense = np.zeros((q.shape[0], v.shape[1]))
     lse = np.zeros(q.shape[0])
     o_dense[held], lse[held] = o_held, lse_held
-    kbar = np.stack([k[b * KV_BLOCK:min(N, (b + 1) * KV_BLOCK)].mean(axis=0)
-                     for b in range(-(-N // KV_BLOCK))])
+    kbar = block_means(k)
     rec = {K: {s: 0.0 for s in SELECTORS} for K in Ks}
     err = {K: {s: 0.0 for s in SELECTORS} for K in Ks}
     for rows in groups:
         s = scale * (q[rows] @ k.T)
         p = np.exp(s - lse[rows][:, None])                 # exact probabilities [n, N]
         mass = p.sum(axis=0)                               # group mass per key
-        pooled = scale * (kbar @ q[rows].mean(axis=0))     # mean-pooled block scores
+        pooled = mean_pooled_scores(q, kbar, rows, scale)  # mean-pooled block scores
         bmass = block_sums(mass, N)
         for K in Ks:
             nblk = max(1, K // KV_BLOCK)

@@ -60,7 +60,7 @@ import numpy as np
 __all__ = [
     "attention_scores", "dense_attention", "probabilities", "groups_from_perm",
     "group_mass", "topk_indices", "select", "retained_mass", "sparse_attention",
-    "residual", "anchor_step", "reuse_step", "principal_direction", "pddp",
+    "residual", "anchor_step", "reuse_step", "principal_direction", "pddp", "sparse_lse", "kept_mass",
     "within_group_variance", "dense_attention_bh", "sparse_attention_bh",
     "select_bh", "pddp_bh", "default_scale",
 ]
@@ -192,6 +192,31 @@ def sparse_attention(q, k, v, perm, idx, C: int, scale: float, residual=None):
         out[members] = (e / e.sum(axis=1, keepdims=True)) @ v[sel]
     if residual is not None:
         out = out + _f64(residual)
+    return out
+
+
+def sparse_lse(q, k, perm, idx, C: int, scale: float) -> np.ndarray:
+    """Per query i of group g: ln sum_{j in idx_g} exp(s_ij), the normaliser
+    of the sparse softmax over the selected keys (natural log).  idx[g] may
+    have any length (a per-group budget)."""
+    q, k = _f64(q), _f64(k)
+    out = np.empty(q.shape[0])
+    for g, members in enumerate(groups_from_perm(perm, C)):
+        s = attention_scores(q[members], k[np.asarray(idx[g], dtype=np.int64)], scale)
+        m = s.max(axis=1)
+        out[members] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out
+
+
+def kept_mass(q, k, lse, perm, idx, C: int, scale: float) -> np.ndarray:
+    """Per query i of group g: sum_{j in idx_g} P_ij, the dense attention mass
+    the selection keeps (the attention recall of one query; ai.info "Main
+    Findings" and "Methodology in Plain English")."""
+    q, k, lse = _f64(q), _f64(k), _f64(lse)
+    out = np.empty(q.shape[0])
+    for g, members in enumerate(groups_from_perm(perm, C)):
+        sel = np.asarray(idx[g], dtype=np.int64)
+        out[members] = probabilities(q[members], k[sel], lse[members], scale).sum(axis=1)
     return out
 
 

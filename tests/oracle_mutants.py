@@ -78,8 +78,14 @@ MUTANTS = {
                                   "s = attention_scores(q[:len(members)], k[sel], scale)"),
     "sign_uses_max_not_abs": (MCS, "i = int(np.argmax(np.abs(vec)))", "i = int(np.argmax(vec))"),
     "projection_on_the_mean": (MCS, "proj = (q[ids] - mu) @ vec", "proj = (q[ids] - mu) @ mu"),
-    "pooled_query_sum_over_all": (DIAG, "pooled = scale * (kbar @ q[rows].mean(axis=0))",
-                                  "pooled = scale * (kbar @ q.mean(axis=0))"),
+    "pooled_query_sum_over_all": (DIAG, "return scale * (kbar @ _f64(q)[rows].mean(axis=0))",
+                                  "return scale * (kbar @ _f64(q).mean(axis=0))"),
+    "sparse_lse_drops_max": (MCS, "out[members] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))",
+                             "out[members] = np.log(np.exp(s - m[:, None]).sum(axis=1))"),
+    "kept_mass_first_keys": (MCS, "out[members] = probabilities(q[members], k[sel], lse[members], scale).sum(axis=1)",
+                             "out[members] = probabilities(q[members], k[:sel.size], lse[members], scale).sum(axis=1)"),
+    "pooled_blocks_budget_off_by_one": (DIAG, "return _top_ids(mean_pooled_scores(q, kbar, rows, scale), max(1, K // KV_BLOCK))",
+                                        "return _top_ids(mean_pooled_scores(q, kbar, rows, scale), max(1, K // KV_BLOCK) + 1)"),
     "block_oracle_uses_first_block": (DIAG, '"block_oracle": _block_keys(_top_ids(bmass, nblk), N),',
                                       '"block_oracle": _block_keys(np.arange(nblk), N),'),
     "perquery_ties_to_larger_id": (DIAG, "keep = gt | (eq & (np.cumsum(eq, axis=1) <= need))",

@@ -186,3 +186,66 @@ def test_tiny_anchor_and_reuse_in_full(mcs):
     for h in range(w.H):
         w_ref = oracle.within_group_variance(qf[0, h], ref_perm[0, h], w.C)
         assert abs(within_group_variance(qf[0, h], perm[0, h], w.C) - w_ref) <= 0.01 * w_ref
+
+
+CHAIN_REUSE_STEPS = {"tiny": 1, "small": 4, "large": 1, "long": 1, "asset3d": 9}
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_chain_at_workload_size(mcs, name):
+    """The anchor step on the GPU's own upstream (GPU grouping -> dense + LSE ->
+    selection on the GPU perm -> sparse -> residual), then the configuration's
+    reuse steps on drifted inputs with the cached perm, ids and residual.  On
+    sampled heads and groups every stage is checked against the oracle fed the
+    GPU's own perm and ids (the long workload's 50-step schedule is run by the
+    benchmark)."""
+    w = synth.WORKLOADS[name]
+    d = _inputs(name)
+    K = accounting.k_from_density(w.densities[0], w.N)
+    G = accounting.num_groups(w.N, w.C)
+    scale = 1 / math.sqrt(w.D)
+    dq, dk, dv = d["dev"]["q"], d["dev"]["k"], d["dev"]["v"]
+    st = mcs.anchor_step(dq, dk, dv, w.C, K, scale)
+    perm = st["perm"].cpu().numpy()
+    assert_perm(perm)
+    o_sp32 = mcs.sparse_attn(dq, dk, dv, st["perm"], st["kv_idx"], w.C, scale=scale, out_dtype=torch.float32)
+    assert torch.equal(o_sp32.to(torch.bfloat16), st["o_sparse"])
+    idx = st["kv_idx"].view(-1, G, K).cpu().numpy()
+    permf = perm.reshape(-1, w.N)
+    o_sp32 = o_sp32.view(-1, w.N, w.D).cpu().numpy()
+    res = st["residual"].view(-1, w.N, w.D)
+    heads = _sample_heads(w)
+    groups = sorted({0, G // 2, G - 1})
+    for bh in heads:
+        q, k, v = (_f64_head(d["x"], t, bh, w) for t in "qkv")
+        # residual: exactly the bf16 rounding of the difference of the two bf16 outputs
+        od = st["out"].view(-1, w.N, w.D)[bh].view(torch.int16).cpu().numpy().view(np.uint16)
+        osp = st["o_sparse"].view(-1, w.N, w.D)[bh].view(torch.int16).cpu().numpy().view(np.uint16)
+        expect = synth.to_bf16_bits((synth.to_f32(od) - synth.to_f32(osp)).astype(np.float32))
+        np.testing.assert_array_equal(res[bh].view(torch.int16).cpu().numpy().view(np.uint16), expect)
+        for g in groups:
+            members = permf[bh, g * w.C:(g + 1) * w.C]
+            _, lse_g = oracle.dense_attention(q[members], k, k, scale)
+            mass = oracle.probabilities(q[members], k, lse_g, scale).sum(axis=0)[None]
+            ref_ids = oracle.topk_indices(mass[0], K)[None]
+            assert_index_sets_match(idx[bh, g:g + 1], ref_ids, mass, K, f"{name} anchor head {bh} group {g}")
+            ref = oracle.sparse_attention(q[members], k, v, np.arange(members.size), idx[bh, g:g + 1], w.C, scale)
+            assert_output_close(o_sp32[bh, members], ref, f"{name} anchor sparse head {bh} group {g}")
+    print(f"[chain] {name}: anchor checked on heads {heads}, groups {groups}", flush=True)
+    x = d["x"]
+    res_f64 = {bh: synth.to_f64(res[bh].view(torch.int16).cpu().numpy().view(np.uint16)) for bh in heads}
+    for t in range(1, CHAIN_REUSE_STEPS[name] + 1):
+        x = synth.drift(name, x, step=t)
+        qt, kt, vt = (to_dev_bf16(x[s]) for s in "qkv")
+        o = mcs.sparse_attn(qt, kt, vt, st["perm"], st["kv_idx"], w.C, residual=st["residual"], scale=scale,
+                            out_dtype=torch.float32).view(-1, w.N, w.D)
+        for bh in heads:
+            q, k, v = (_f64_head(x, s, bh, w) for s in "qkv")
+            ob = o[bh].cpu().numpy()
+            for g in groups:
+                members = permf[bh, g * w.C:(g + 1) * w.C]
+                ref = oracle.sparse_attention(q[members], k, v, np.arange(members.size), idx[bh, g:g + 1], w.C,
+                                              scale, residual=res_f64[bh][members])
+                assert_output_close(ob[members], ref, f"{name} reuse step {t} head {bh} group {g}")
+        del qt, kt, vt, o
+    print(f"[chain] {name}: {CHAIN_REUSE_STEPS[name]} reuse steps checked", flush=True)

@@ -234,3 +234,28 @@ def test_scoring_a_sample_of_groups_averages_over_their_queries():
     for s in dg.SELECTORS:
         parts = [dg.diagnose_groups(q, k, v, [g], [64], 0.4)[64][s]["recall"] * len(g) for g in groups]
         assert sum(parts) / N == pytest.approx(full[s]["recall"], rel=1e-12)
+
+
+def test_mean_pooled_blocks_closed_form():
+    # keys in 4 blocks of 64 whose means point along e0, e1, -e0 and 2 e1; a
+    # query block with mean 3 e1 + e0 scores them 3s, ... so with budget 128
+    # (two blocks) the blocks are {1, 3} and with 64 just {3}
+    from oracle import diagnostics as dg
+    N, D = 256, 4
+    k = np.zeros((N, D))
+    means = [np.eye(D)[0], np.eye(D)[1], -np.eye(D)[0], 2 * np.eye(D)[1]]
+    rng = np.random.default_rng(33)
+    for b, m in enumerate(means):
+        noise = rng.standard_normal((64, D))
+        noise -= noise.mean(axis=0)                    # block mean exactly m
+        k[64 * b:64 * (b + 1)] = m + 0.1 * noise
+    kbar = dg.block_means(k)
+    np.testing.assert_allclose(kbar, np.stack(means), atol=1e-14)
+    q = np.tile(np.array([1.0, 3.0, 0.0, 0.0]), (10, 1))
+    np.testing.assert_allclose(dg.mean_pooled_scores(q, kbar, np.arange(10), 0.5),
+                               0.5 * np.array([1.0, 3.0, -1.0, 6.0]), atol=1e-14)
+    assert dg.mean_pooled_blocks(q, kbar, np.arange(10), 128, 0.5).tolist() == [1, 3]
+    assert dg.mean_pooled_blocks(q, kbar, np.arange(10), 64, 0.5).tolist() == [3]
+    # ties go to the smaller block id
+    kt = np.zeros((192, D))
+    assert dg.mean_pooled_blocks(q, dg.block_means(kt), np.arange(10), 128, 0.5).tolist() == [0, 1]

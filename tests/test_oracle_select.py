@@ -110,3 +110,49 @@ def test_select_bh_shapes():
     perm = np.stack([np.stack([np.arange(30), np.arange(30)[::-1]])])
     idx, mass = oracle.select_bh(q, k, lse, perm, 8, 5, 0.3)
     assert idx.shape == (1, 2, 4, 5) and mass.shape == (1, 2, 4, 30)
+
+
+# ---- per-query selection statistics: sparse LSE and kept (recalled) mass ----
+
+def test_sparse_lse_and_kept_mass_two_keys():
+    # one query, keys with scores 1 and 3 (scale 1): selecting key 0 keeps
+    # e/(e + e^3) of the mass, and its sparse LSE is the score itself
+    q = np.array([[1.0, 0.0]])
+    k = np.array([[1.0, 0.0], [3.0, 0.0]])
+    _, lse = oracle.dense_attention(q, k, k, 1.0)
+    assert oracle.sparse_lse(q, k, np.array([0]), [np.array([0])], 1, 1.0)[0] == pytest.approx(1.0, abs=1e-15)
+    kept = oracle.kept_mass(q, k, lse, np.array([0]), [np.array([0])], 1, 1.0)[0]
+    assert kept == pytest.approx(np.e / (np.e + np.e ** 3), rel=1e-14)
+
+
+def test_sparse_lse_full_budget_is_dense_lse_and_recall_is_one():
+    rng = np.random.default_rng(31)
+    N, D, C = 70, 8, 16
+    q, k = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    perm = rng.permutation(N)
+    G = -(-N // C)
+    full = [np.arange(N)] * G
+    _, lse = oracle.dense_attention(q, k, k, 0.4)
+    np.testing.assert_allclose(oracle.sparse_lse(q, k, perm, full, C, 0.4), lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.kept_mass(q, k, lse, perm, full, C, 0.4), 1.0, rtol=0, atol=1e-12)
+
+
+def test_kept_mass_matches_lse_gap_and_group_retained_mass():
+    rng = np.random.default_rng(32)
+    N, D, C, K = 90, 6, 16, 20
+    q, k = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    perm = rng.permutation(N)
+    _, lse = oracle.dense_attention(q, k, k, 0.5)
+    idx, mass = oracle.select(q, k, lse, perm, C, K, 0.5)
+    kept = oracle.kept_mass(q, k, lse, perm, idx, C, 0.5)
+    # the same quantity through the sparse normaliser
+    np.testing.assert_allclose(kept, np.exp(oracle.sparse_lse(q, k, perm, idx, C, 0.5) - lse), rtol=1e-12)
+    # summed over a group it is the group's retained mass
+    rho = oracle.retained_mass(mass, idx)
+    for g, members in enumerate(oracle.groups_from_perm(perm, C)):
+        assert kept[members].sum() == pytest.approx(rho[g], rel=1e-12)
+    assert (kept <= 1 + 1e-12).all()
+    # per-group budgets of any length, monotone in the budget
+    short = [ids[: 5 + g] for g, ids in enumerate(idx)]
+    kept_short = oracle.kept_mass(q, k, lse, perm, short, C, 0.5)
+    assert (kept_short <= kept + 1e-15).all()

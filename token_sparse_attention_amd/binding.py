@@ -43,6 +43,11 @@ _SIGS = {
     "mcs_dense_attn_f32out": ([_P, _P, _P, _P, _P, Dims, _F, _P], _I32),
     "mcs_sparse_attn_f32out": ([_P, _P, _P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P], _I32),
     "mcs_residual_update": ([_P, _P, _P, _I64, _P], _I32),
+    "mcs_sparse_attn_ex": ([_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, Dims, _I32, _I32, _F, _P], _I32),
+    "mcs_select_blocks": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
+    "mcs_select_blocks_workspace": ([Dims], _SZ),
+    "mcs_query_quality": ([_P, _P, _P, _P, _P, _P, _P, Dims, _P], _I32),
+    "mcs_row_sums": ([_P, _P, _I64, _I64, _P], _I32),
     "mcs_select": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
     "mcs_select_two_pass": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
     "mcs_select_workspace": ([Dims, _I32, _I32], _SZ),
@@ -191,6 +196,69 @@ def sparse_attn(q, k, v, perm, kv_idx, C, residual=None, scale=None, out=None, o
     fn = _lib.mcs_sparse_attn_f32out if out.dtype == torch.float32 else _lib.mcs_sparse_attn
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(kv_idx), _ptr(residual), _ptr(out), dims_of(q),
               C, K, scale, _stream(q)))
+    return out
+
+
+def sparse_attn_ex(q, k, v, perm, kv_idx, C, kv_count=None, residual=None, scale=None, want_lse=False,
+                   out=None, out_dtype=torch.bfloat16):
+    """mcs_sparse_attn_ex: sparse_attn with optional per-group key counts and the
+    per-query LSE over the selected keys.  Returns out, or (out, lse)."""
+    _qkv(q, k, v)
+    B, H, N, D = q.shape
+    _like(perm, "perm", torch.int32, (B, H, N), q.device)
+    _need(kv_idx, "kv_idx", torch.int32, 4)
+    G = num_groups(N, C)
+    if tuple(kv_idx.shape[:3]) != (B, H, G) or kv_idx.device != q.device:
+        raise ValueError(f"kv_idx must be [B, H, G={G}, K] on {q.device} (got {tuple(kv_idx.shape)})")
+    if kv_count is not None:
+        _like(kv_count, "kv_count", torch.int32, (B, H, G), q.device)
+    if residual is not None:
+        _like(residual, "residual", torch.bfloat16, q.shape, q.device)
+    K = kv_idx.shape[3]
+    scale = default_scale(D) if scale is None else scale
+    out = _out(q, out, out_dtype)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if want_lse else None
+    _check(_lib.mcs_sparse_attn_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(kv_idx), _ptr(kv_count),
+                                   _ptr(residual), _ptr(out), int(out.dtype == torch.float32), _ptr(lse),
+                                   dims_of(q), C, K, scale, _stream(q)))
+    return (out, lse) if want_lse else out
+
+
+def select_blocks(q, k, perm, C, K, scale=None, workspace=None):
+    """mcs_select_blocks: mean-pooled block selection -> (kv_idx [B,H,G,K], kv_count [B,H,G])."""
+    _qkv(q, k)
+    B, H, N, D = q.shape
+    _like(perm, "perm", torch.int32, (B, H, N), q.device)
+    G = num_groups(N, C)
+    scale = default_scale(D) if scale is None else scale
+    kv_idx = torch.empty((B, H, G, K), dtype=torch.int32, device=q.device)
+    kv_count = torch.empty((B, H, G), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        need = int(_lib.mcs_select_blocks_workspace(dims_of(q)))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(_lib.mcs_select_blocks(_ptr(q), _ptr(k), _ptr(perm), _ptr(kv_idx), _ptr(kv_count), dims_of(q), C, K,
+                                  scale, _ptr(workspace), workspace.numel(), _stream(q)))
+    return kv_idx, kv_count
+
+
+def query_quality(lse_dense, lse_sparse, o_dense, o_sparse):
+    """mcs_query_quality: per-query recall, L1 distance and dense L1 norm (float32 [B,H,N] each)."""
+    _need(o_dense, "o_dense", torch.float32, 4)
+    B, H, N, D = o_dense.shape
+    _like(o_sparse, "o_sparse", torch.float32, o_dense.shape, o_dense.device)
+    _like(lse_dense, "lse_dense", torch.float32, (B, H, N), o_dense.device)
+    _like(lse_sparse, "lse_sparse", torch.float32, (B, H, N), o_dense.device)
+    recall, l1, l1_ref = (torch.empty((B, H, N), dtype=torch.float32, device=o_dense.device) for _ in range(3))
+    _check(_lib.mcs_query_quality(_ptr(lse_dense), _ptr(lse_sparse), _ptr(o_dense), _ptr(o_sparse), _ptr(recall),
+                                  _ptr(l1), _ptr(l1_ref), Dims(B, H, N, D), _stream(o_dense)))
+    return recall, l1, l1_ref
+
+
+def row_sums(x):
+    """mcs_row_sums: fp64 sums of the rows of a contiguous float32 [rows, n] tensor."""
+    _need(x, "x", torch.float32, 2)
+    out = torch.empty(x.shape[0], dtype=torch.float64, device=x.device)
+    _check(_lib.mcs_row_sums(_ptr(x), _ptr(out), x.shape[0], x.shape[1], _stream(x)))
     return out
 
 

@@ -133,8 +133,8 @@ static mcs_status dense_common(const char* fn, const uint16_t* q, const uint16_t
   if ((st = check_dims(fn, d)) != MCS_OK) return st;
   if ((st = check_scale(fn, scale)) != MCS_OK) return st;
   const int C = 128;   // query rows per workgroup
-  return launched(fn, mcs::run_attention(q, k, v, nullptr, nullptr, nullptr, o, out_f32, lse, d.B,
-                                         d.H, d.N, d.D, C, d.N, scale, (hipStream_t)stream));
+  return launched(fn, mcs::run_attention(q, k, v, nullptr, nullptr, nullptr, nullptr, o, out_f32, lse,
+                                         d.B, d.H, d.N, d.D, C, d.N, scale, (hipStream_t)stream));
 }
 
 mcs_status mcs_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
@@ -149,38 +149,51 @@ mcs_status mcs_dense_attn_f32out(const uint16_t* q, const uint16_t* k, const uin
 
 static mcs_status sparse_common(const char* fn, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
-                                const uint16_t* residual, void* o, bool out_f32, mcs_dims d,
-                                int32_t C, int32_t K, float scale, void* stream) {
+                                const int32_t* kv_count, const uint16_t* residual, void* o,
+                                bool out_f32, float* lse, mcs_dims d, int32_t C, int32_t K,
+                                float scale, void* stream) {
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
   REQUIRE_PTR(perm);
   REQUIRE_PTR(kv_idx);
+  OPTIONAL_PTR(kv_count);
   OPTIONAL_PTR(residual);
+  OPTIONAL_PTR(lse);
   REQUIRE_PTR(o);
   mcs_status st;
   if ((st = check_dims(fn, d)) != MCS_OK) return st;
   if ((st = check_group_size(fn, C)) != MCS_OK) return st;
   if ((st = check_budget(fn, d, C, K)) != MCS_OK) return st;
   if ((st = check_scale(fn, scale)) != MCS_OK) return st;
-  return launched(fn, mcs::run_attention(q, k, v, perm, kv_idx, residual, o, out_f32, nullptr, d.B,
-                                         d.H, d.N, d.D, C, K, scale, (hipStream_t)stream));
+  if (residual != nullptr && lse != nullptr)
+    return fail(MCS_E_ARG, "%s: residual and lse cannot both be given", fn);
+  return launched(fn, mcs::run_attention(q, k, v, perm, kv_idx, kv_count, residual, o, out_f32, lse,
+                                         d.B, d.H, d.N, d.D, C, K, scale, (hipStream_t)stream));
 }
 
 mcs_status mcs_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const int32_t* perm, const int32_t* kv_idx, const uint16_t* residual,
                            uint16_t* o, mcs_dims d, int32_t C, int32_t K, float scale,
                            void* stream) {
-  return sparse_common("mcs_sparse_attn", q, k, v, perm, kv_idx, residual, o, false, d, C, K, scale,
-                       stream);
+  return sparse_common("mcs_sparse_attn", q, k, v, perm, kv_idx, nullptr, residual, o, false, nullptr,
+                       d, C, K, scale, stream);
 }
 
 mcs_status mcs_sparse_attn_f32out(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   const int32_t* perm, const int32_t* kv_idx,
                                   const uint16_t* residual, float* o, mcs_dims d, int32_t C,
                                   int32_t K, float scale, void* stream) {
-  return sparse_common("mcs_sparse_attn_f32out", q, k, v, perm, kv_idx, residual, o, true, d, C, K,
-                       scale, stream);
+  return sparse_common("mcs_sparse_attn_f32out", q, k, v, perm, kv_idx, nullptr, residual, o, true,
+                       nullptr, d, C, K, scale, stream);
+}
+
+mcs_status mcs_sparse_attn_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* perm, const int32_t* kv_idx, const int32_t* kv_count,
+                              const uint16_t* residual, void* o, int32_t o_f32, float* lse,
+                              mcs_dims d, int32_t C, int32_t K, float scale, void* stream) {
+  return sparse_common("mcs_sparse_attn_ex", q, k, v, perm, kv_idx, kv_count, residual, o, o_f32 != 0,
+                       lse, d, C, K, scale, stream);
 }
 
 mcs_status mcs_residual_update(const uint16_t* o_dense, const uint16_t* o_sparse,
@@ -324,6 +337,67 @@ mcs_status mcs_group_noalloc(const uint16_t* q, int32_t* perm, mcs_dims d, int32
     if (e != hipSuccess) return launched(fn, e);
   }
   return ok();
+}
+
+size_t mcs_select_blocks_workspace(mcs_dims d) {
+  if (d.B < 1 || d.H < 1 || d.N < 1 || (d.D != 64 && d.D != 128)) return 0;
+  return mcs::block_select_ws_bytes(d.B * d.H, d.N, d.D);
+}
+
+mcs_status mcs_select_blocks(const uint16_t* q, const uint16_t* k, const int32_t* perm, int32_t* kv_idx,
+                             int32_t* kv_count, mcs_dims d, int32_t C, int32_t K, float scale, void* ws,
+                             size_t ws_bytes, void* stream) {
+  const char* fn = "mcs_select_blocks";
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(perm);
+  REQUIRE_PTR(kv_idx);
+  REQUIRE_PTR(kv_count);
+  mcs_status st;
+  if ((st = check_dims(fn, d)) != MCS_OK) return st;
+  if ((st = check_group_size(fn, C)) != MCS_OK) return st;
+  if ((st = check_scale(fn, scale)) != MCS_OK) return st;
+  const int64_t NB = ((int64_t)d.N + 63) / 64;
+  if (NB > mcs::kMaxKeyBlocks)
+    return fail(MCS_E_SHAPE, "%s: N = %d gives %lld key blocks, more than %d", fn, d.N, (long long)NB,
+                mcs::kMaxKeyBlocks);
+  if (K < 64 || K % 64 != 0 || K / 64 > NB)
+    return fail(MCS_E_BUDGET, "%s: K must be a multiple of 64 in [64, 64 * %lld] (got %d)", fn,
+                (long long)NB, K);
+  const size_t need = mcs::block_select_ws_bytes(d.B * d.H, d.N, d.D);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MCS_E_WORKSPACE, "%s: workspace of %zu bytes given, at least %zu needed", fn,
+                ws == nullptr ? (size_t)0 : ws_bytes, need);
+  if (!aligned16(ws)) return fail(MCS_E_ALIGN, "%s: ws is not 16-byte aligned", fn);
+  return launched(fn, mcs::run_block_select(q, k, perm, kv_idx, kv_count, d.B * d.H, d.N, d.D, C, K, scale,
+                                            ws, (hipStream_t)stream));
+}
+
+mcs_status mcs_query_quality(const float* lse_dense, const float* lse_sparse, const float* o_dense,
+                             const float* o_sparse, float* recall, float* l1, float* l1_ref, mcs_dims d,
+                             void* stream) {
+  const char* fn = "mcs_query_quality";
+  REQUIRE_PTR(lse_dense);
+  REQUIRE_PTR(lse_sparse);
+  REQUIRE_PTR(o_dense);
+  REQUIRE_PTR(o_sparse);
+  REQUIRE_PTR(recall);
+  REQUIRE_PTR(l1);
+  REQUIRE_PTR(l1_ref);
+  mcs_status st;
+  if ((st = check_dims(fn, d)) != MCS_OK) return st;
+  return launched(fn, mcs::run_query_quality(lse_dense, lse_sparse, o_dense, o_sparse, recall, l1, l1_ref,
+                                             (int64_t)d.B * d.H * d.N, d.D, (hipStream_t)stream));
+}
+
+mcs_status mcs_row_sums(const float* x, double* out, int64_t rows, int64_t n, void* stream) {
+  const char* fn = "mcs_row_sums";
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(out);
+  if (rows < 1 || n < 1 || rows > INT32_MAX)
+    return fail(MCS_E_SHAPE, "%s: rows must be in [1, 2^31) and n >= 1 (got %lld, %lld)", fn, (long long)rows,
+                (long long)n);
+  return launched(fn, mcs::run_row_sums(x, out, rows, n, (hipStream_t)stream));
 }
 
 const char* mcs_status_string(mcs_status s) {

@@ -34,7 +34,8 @@
 //     product (v_dot2c_f32_bf16 against (1, 1)), so its error scales with
 //     |v_j - o| instead of |v_j|; the LSE uses the exact fp32 sum.
 //   * Epilogue: O = O^T / l (+ residual), bf16 or fp32, scattered to the query
-//     rows; lse = (m + log2 l) * ln 2 for the dense pass.
+//     rows; lse = (m + log2 l) * ln 2 (the dense pass, or on request the
+//     sparse one over its selected keys).
 #include <type_traits>
 
 #include "mcs_common.h"
@@ -63,6 +64,7 @@ struct AttnParams {
   const uint16_t* v;
   const int32_t* perm;    // sparse only
   const int32_t* kv_idx;  // sparse only
+  const int32_t* kv_count;  // sparse, optional: keys used per group (first ids)
   const uint16_t* res;    // optional residual
   void* o;                // bf16 or fp32 output
   float* lse;             // optional (dense)
@@ -119,7 +121,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   for (int t = 0; t < KSTEPS; ++t)
     qf[t] = as_bf16x8(qvalid ? ldg16(qh + (size_t)qrow * D + 16 * t + 8 * hh) : zero_u32x4());
 
-  const int nkeys = SPARSE ? p.K : p.N;
+  int nkeys = SPARSE ? p.K : p.N;
+  if (SPARSE && p.kv_count != nullptr) {
+    const int c = __builtin_amdgcn_readfirstlane(p.kv_count[(size_t)bh * p.G + g]);
+    nkeys = c < 1 ? 1 : (c > p.K ? p.K : c);
+  }
   const int ntiles = (nkeys + KT - 1) / KT;
   const int32_t* __restrict__ ids = SPARSE ? p.kv_idx + ((size_t)bh * p.G + g) * p.K : nullptr;
 
@@ -429,6 +435,7 @@ static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
 template <int D, int NW, bool OUTF32>
 static hipError_t dispatch_attn(const AttnParams& p, bool sparse, bool res, bool lse, hipStream_t s) {
   if (sparse) {
+    if (lse) return launch_attn<D, NW, true, false, true, OUTF32>(p, s);   // no residual (checked)
     return res ? launch_attn<D, NW, true, true, false, OUTF32>(p, s)
                : launch_attn<D, NW, true, false, false, OUTF32>(p, s);
   }
@@ -448,11 +455,11 @@ static hipError_t dispatch_shape(const AttnParams& p, int D, int C, bool sparse,
 }
 
 hipError_t run_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* perm, const int32_t* kv_idx, const uint16_t* res,
-                         void* o, bool out_f32, float* lse, int B, int H, int N, int D, int C, int K,
-                         float scale, hipStream_t s) {
+                         const int32_t* perm, const int32_t* kv_idx, const int32_t* kv_count,
+                         const uint16_t* res, void* o, bool out_f32, float* lse, int B, int H, int N,
+                         int D, int C, int K, float scale, hipStream_t s) {
   AttnParams p;
-  p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.res = res;
+  p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.kv_count = kv_count; p.res = res;
   p.o = o; p.lse = lse;
   p.N = N; p.C = C; p.K = K; p.G = (N + C - 1) / C; p.BH = B * H;
   p.sl2 = scale * kLog2e;

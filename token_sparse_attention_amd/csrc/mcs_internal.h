@@ -8,11 +8,11 @@
 namespace mcs {
 
 // Dense (kv_idx == nullptr, optional lse) or sparse (perm and kv_idx given,
-// optional residual) attention.
+// optional per-group key counts, optional residual or lse, not both) attention.
 hipError_t run_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const int32_t* perm, const int32_t* kv_idx, const uint16_t* res,
-                         void* o, bool out_f32, float* lse, int B, int H, int N, int D, int C,
-                         int K, float scale, hipStream_t s);
+                         const int32_t* perm, const int32_t* kv_idx, const int32_t* kv_count,
+                         const uint16_t* res, void* o, bool out_f32, float* lse, int B, int H,
+                         int N, int D, int C, int K, float scale, hipStream_t s);
 
 hipError_t run_residual(const uint16_t* od, const uint16_t* osp, uint16_t* r, int64_t n,
                         hipStream_t s);
@@ -32,6 +32,16 @@ hipError_t run_select_fused(const uint16_t* q, const uint16_t* k, const float* l
 // Top-K of non-negative rows (ties to the smaller id, ids ascending).
 hipError_t run_topk(const float* scores, int32_t* idx, int64_t rows, int n, int K,
                     hipStream_t s);
+
+// Selection diagnostics and the block-sparse comparison (diag.hip).
+constexpr int kMaxKeyBlocks = 4096;   // 64-key blocks per head the block selector holds on chip
+size_t block_select_ws_bytes(int BH, int N, int D);
+hipError_t run_block_select(const uint16_t* q, const uint16_t* k, const int32_t* perm, int32_t* kv_idx,
+                            int32_t* kv_count, int BH, int N, int D, int C, int K, float scale, void* ws,
+                            hipStream_t s);
+hipError_t run_query_quality(const float* lse_d, const float* lse_s, const float* od, const float* os,
+                             float* recall, float* l1, float* l1ref, int64_t rows, int D, hipStream_t s);
+hipError_t run_row_sums(const float* x, double* out, int64_t rows, int64_t n, hipStream_t s);
 
 // Median-split PDDP.
 struct GroupPlan {
