@@ -14,9 +14,14 @@ The headline metric is the token-sparse attention speedup over this library's
 own dense attention at the same shape (reuse-step sparse kernel vs the dense
 kernel without LSE; the anchor's dense pass with LSE is reported beside it),
 with the sparse kernel's MFMA-roofline fraction at the density-scaled FLOP
-count 4*B*H*N*K*D.  One JSON line is printed.  --all-workloads measures every
-workload and density instead (one line each), with the anchor-path cost and
-the 50-step schedule with an anchor every 10 steps.
+count 4*B*H*N*K*D, and beside it vanilla block-sparse attention at the same
+budget (mean-pooled block selection, same sparse kernel).  One JSON line is
+printed.  --all-workloads measures every workload and density instead (one
+line each, with the anchor-path cost and the 50-step schedule with an anchor
+every 10 steps by formula), then runs every workload's step schedule on
+drifted inputs (the long workload: 50 steps, an anchor every 10).
+--diagnostics scores the token and block selections of every workload by
+attention recall and relative L1 error of the output, on the GPU.
 """
 from __future__ import annotations
 
@@ -55,7 +60,11 @@ def parse():
     ap.add_argument("--torch-sdpa", action="store_true",
                     help="also time torch's scaled_dot_product_attention (flash backend) on the dense shape")
     ap.add_argument("--all-workloads", action="store_true",
-                    help="every workload and density (one JSON line each) instead of the headline one")
+                    help="every workload and density (one JSON line each) instead of the headline one, "
+                         "then every workload's step schedule, run")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="attention recall and output error of the token and block selections on the GPU, "
+                         "every workload at densities 0.1 / 0.2 / 0.3")
     return ap.parse_args()
 
 
@@ -68,11 +77,13 @@ def cpu_baseline(args, w, x, K, scale):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
     from token_sparse_attention_amd import synth
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        blas = 1
+    cores = min(affinity, blas)        # the oracle's matrix products run on the BLAS threads
     q = synth.to_f64(x["q"][0, 0])
     k = synth.to_f64(x["k"][0, 0])
     v = synth.to_f64(x["v"][0, 0])
@@ -103,8 +114,21 @@ def cpu_baseline(args, w, x, K, scale):
         "sparse_s_extrapolated": round(sparse_per_row * n_rows, 1),
         "sparse_tflops": round(4.0 * sub.size * K * w.D / t_sparse / 1e12, 4),
         "dense_tflops": round(4.0 * rows * w.N * w.D / t_dense / 1e12, 4),
-        "cpu": platform.processor() or platform.machine(),
+        "affinity_cpus": affinity,
+        "blas_threads": blas,
+        "cpu": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return platform.processor() or platform.machine()
 
 
 def measured_traffic(workload: str, kernel_prefix: str):
@@ -161,6 +185,49 @@ def torch_sdpa_ms(q, k, v, reps: int):
         return round(float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), 4)
     except Exception as ex:  # no flash backend for this device or shape
         return f"unavailable: {str(ex)[:160]}"
+
+
+def _mean_ms(fn, reps: int) -> float:
+    import torch
+    fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        ev[i].record()
+        fn()
+    ev[reps].record()
+    torch.cuda.synchronize()
+    return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+
+def measure_bsa(q0, k0, v0, q1, k1, v1, res, C, K, scale, reps: int, dense_nolse_ms: float) -> dict:
+    """Vanilla block-sparse attention at the same budget, the pages' efficiency
+    reference: contiguous query blocks of C, the K/64 key blocks of best
+    mean-pooled score (mcs_select_blocks), then the same sparse kernel over
+    the kept blocks' tokens with the residual epilogue (mcs_sparse_attn_ex)."""
+    import torch
+
+    from token_sparse_attention_amd import binding
+    B, H, N, D = q0.shape
+    ident = torch.arange(N, dtype=torch.int32, device=q0.device).expand(B, H, N).contiguous()
+    ws = torch.empty(max(int(binding._lib.mcs_select_blocks_workspace(binding.dims_of(q0))), 16),
+                     dtype=torch.uint8, device=q0.device)
+    holder = {}
+
+    def select():
+        holder["sel"] = binding.select_blocks(q0, k0, ident, C, K, scale, workspace=ws)
+
+    select_ms = _mean_ms(select, reps)
+    bidx, bcnt = holder["sel"]
+    out = torch.empty_like(q1)
+    sparse_ms = _mean_ms(lambda: binding.sparse_attn_ex(q1, k1, v1, ident, bidx, C, kv_count=bcnt, residual=res,
+                                                        scale=scale, out=out), reps)
+    keys = float(bcnt.double().mean().item())          # real keys per group (short last block)
+    flops = 4.0 * B * H * N * keys * D
+    return {"select_ms": round(select_ms, 4), "sparse_ms": round(sparse_ms, 4),
+            "mean_keys_per_group": round(keys, 1),
+            "tflops": round(flops / (sparse_ms * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(flops / (sparse_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "efficiency_vs_ideal": round(dense_nolse_ms * keys / N / sparse_ms, 4)}
 
 
 def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
@@ -253,6 +320,7 @@ def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
     dense_nolse_ms = float(np.mean([e0[i].elapsed_time(e0[i + 1]) for i in range(reps)]))
     speedup = dense_nolse_ms / ms["sparse_reuse"]
     torch_sdpa = torch_sdpa_ms(q0, k0, v0, reps) if args.torch_sdpa else None
+    bsa = measure_bsa(q0, k0, v0, q1, k1, v1, res, w.C, K, scale, reps, dense_nolse_ms)
 
     sparse_flops = accounting.sparse_flops(B, H, N, K, D)
     dense_flops = accounting.dense_flops(B, H, N, D)
@@ -295,16 +363,20 @@ def measure(args, workload: str, density, steps: int, warmup: int) -> dict:
         "efficiency_vs_ideal": round(speedup * K / N, 4),
         "dense_tflops": round(dense_flops / (ms["dense_lse"] * 1e-3) / 1e12, 2),
         "select_tflops": round(accounting.select_flops(B, H, N, D) / (ms["select"] * 1e-3) / 1e12, 2),
+        "block_sparse": bsa,
     }
     util = measured_util(workload, f"attn_kernel<{D}, {w.C // 32}, true, true")
     if util is not None:
-        # the clock this kernel ran at under the counters (GRBM_GUI_ACTIVE over
+        # context from the committed counter profile (another run, same kernel
+        # sources): the clock this kernel ran at there (GRBM_GUI_ACTIVE over
         # the dispatch time) and the bf16 MFMA peak at that clock
         peak_clk = PEAK_BF16_TFLOPS * util["clock_ghz"] / 2.4
-        out["roofline"].update({"measured_clock_ghz": round(util["clock_ghz"], 3),
-                                "peak_at_measured_clock": round(peak_clk, 1),
-                                "frac_at_measured_clock": round(achieved / peak_clk, 4),
-                                "mfma_busy_counter": round(util["mfma_busy"], 4)})
+        out["roofline"]["from_profile"] = {
+            "source": f"profiles/pmc_util_{workload}.json (a separate rocprofv3 --pmc run)",
+            "clock_ghz": round(util["clock_ghz"], 3),
+            "peak_at_that_clock": round(peak_clk, 1),
+            "frac_at_that_clock": round(achieved / peak_clk, 4),
+            "mfma_busy": round(util["mfma_busy"], 4)}
     # anchor-path cost, and the schedule of the long-video setting: 50 steps
     # with an anchor every 10 (5 anchors, 45 reuse steps)
     t_anchor = sum(ms[k] for k in ("group", "dense_lse", "select", "sparse_anchor", "residual"))
@@ -392,6 +464,135 @@ def measure_offload(args, workload: str, layers: int, steps: int) -> dict:
 
 ALL_CONFIGS = [("tiny", 0.25), ("small", 0.20), ("large", 0.20), ("long", 0.25), ("long", 0.15), ("asset3d", 0.15)]
 
+# the configurations' step schedules: (steps, anchor steps); the others reuse
+# the last anchor's groups, ids and residual on drifted inputs
+SCHEDULES = {"tiny": (2, (0,)), "small": (5, (0,)), "large": (2, (0,)), "long": (50, (0, 10, 20, 30, 40)),
+             "asset3d": (10, (0,))}
+
+
+def measure_schedule(args, workload: str) -> dict:
+    """Runs the workload's schedule (every density at once, on the same drifted
+    inputs): anchor steps run the whole anchor path, the others one token-sparse
+    launch with the cached residual.  Each step's GPU time is taken with HIP
+    events; generating the next step's inputs on the host is not timed."""
+    import torch
+
+    from token_sparse_attention_amd import accounting, binding, synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[workload]
+    nsteps, anchors = SCHEDULES[workload]
+    scale = 1.0 / math.sqrt(w.D)
+    Ks = [accounting.k_from_density(s, w.N) for s in w.densities]
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = synth.generate(workload)
+    q, k, v = (dev_bf16(x[t]) for t in "qkv")
+    shape = tuple(q.shape)
+    B, H, N, D = shape
+    G = accounting.num_groups(N, w.C)
+    perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    o_dense = torch.empty_like(q)
+    o_sp = torch.empty_like(q)
+    o = torch.empty_like(q)
+    ws_group = torch.empty(max(binding.group_workspace_bytes(shape, w.C), 16), dtype=torch.uint8, device=dev)
+    ws_sel = torch.empty(binding.select_workspace_bytes(shape, w.C, max(Ks), all_heads=True), dtype=torch.uint8,
+                         device=dev)
+    state = [{"idx": torch.empty((B, H, G, K), dtype=torch.int32, device=dev), "res": torch.empty_like(q),
+              "anchor_ms": [], "reuse_ms": []} for K in Ks]
+    dense_ms = _mean_ms(lambda: binding.dense_attn(q, k, v, scale, out=o_dense), 3)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t_host = time.time()
+    for t in range(nsteps):
+        if t > 0:
+            x = synth.drift(workload, x, step=t)
+            for dst, name in ((q, "q"), (k, "k"), (v, "v")):
+                dst.copy_(dev_bf16(x[name]))
+        for K, stt in zip(Ks, state):
+            ev[0].record()
+            if t in anchors:
+                binding.group(q, w.C, out=perm, workspace=ws_group)
+                binding.dense_attn(q, k, v, scale, want_lse=True, out=o_dense, lse=lse)
+                binding.select(q, k, lse, perm, w.C, K, scale, out=stt["idx"], workspace=ws_sel)
+                binding.sparse_attn(q, k, v, perm, stt["idx"], w.C, scale=scale, out=o_sp)
+                binding.residual_update(o_dense, o_sp, out=stt["res"])
+            else:
+                binding.sparse_attn(q, k, v, perm, stt["idx"], w.C, residual=stt["res"], scale=scale, out=o)
+            ev[1].record()
+            torch.cuda.synchronize()
+            (stt["anchor_ms"] if t in anchors else stt["reuse_ms"]).append(ev[0].elapsed_time(ev[1]))
+    log(args, f"[bench] {workload} schedule of {nsteps} steps in {time.time() - t_host:.1f}s")
+    out = {"workload": workload, "steps": nsteps, "anchor_steps": list(anchors), "dense_nolse_ms": round(dense_ms, 4),
+           "densities": {}}
+    for s_, K, stt in zip(w.densities, Ks, state):
+        total = sum(stt["anchor_ms"]) + sum(stt["reuse_ms"])
+        out["densities"][str(s_)] = {
+            "K": K,
+            "anchor_ms_mean": round(float(np.mean(stt["anchor_ms"])), 4),
+            "reuse_ms_mean": round(float(np.mean(stt["reuse_ms"])), 4) if stt["reuse_ms"] else None,
+            "mean_step_ms": round(total / nsteps, 4),
+            "speedup_vs_dense_steps": round(dense_ms * nsteps / total, 4),
+            "anchor_overhead_vs_dense": round(sum(a - dense_ms for a in stt["anchor_ms"]) / (nsteps * dense_ms), 4)}
+    del x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+DIAG_DENSITIES = (0.1, 0.2, 0.3)
+
+
+def measure_diagnostics(args, workload: str) -> list:
+    """Attention recall and relative L1 error of the output, on the GPU, for the
+    library's own selection (PDDP groups, exact token selection) and for
+    vanilla block-sparse attention (contiguous query blocks, mean-pooled key
+    blocks) at densities 0.1 / 0.2 / 0.3 of one workload's anchor inputs.
+    Every query of every head is scored.  Budgets K = 128*floor(s*N/128), at
+    least 128."""
+    import torch
+
+    from token_sparse_attention_amd import accounting, binding, synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[workload]
+    scale = 1.0 / math.sqrt(w.D)
+    x = synth.generate(workload)
+    q, k, v = (torch.from_numpy(x[t].view(np.int16)).view(torch.bfloat16).to(dev) for t in "qkv")
+    del x
+    B, H, N, D = q.shape
+    perm = binding.group(q, w.C)
+    ident = torch.arange(N, dtype=torch.int32, device=dev).expand(B, H, N).contiguous()
+    od, lse = binding.dense_attn(q, k, v, scale, want_lse=True, out_dtype=torch.float32)
+    rows = B * H * N
+
+    def quality(o_s, lse_s):
+        rec, l1, l1r = binding.query_quality(lse, lse_s, od, o_s)
+        sums = binding.row_sums(torch.stack([rec.view(-1), l1.view(-1), l1r.view(-1)])).cpu().numpy()
+        return {"recall": round(float(sums[0] / rows), 4), "rel_l1": round(float(sums[1] / sums[2]), 4)}
+
+    out = []
+    for s_ in DIAG_DENSITIES:
+        K = max(128, accounting.k_from_density(s_, N))
+        idx = binding.select(q, k, lse, perm, w.C, K, scale)
+        o_s, lse_s = binding.sparse_attn_ex(q, k, v, perm, idx, w.C, scale=scale, want_lse=True,
+                                            out_dtype=torch.float32)
+        token = quality(o_s, lse_s)
+        del idx
+        bidx, bcnt = binding.select_blocks(q, k, ident, w.C, K, scale)
+        o_b, lse_b = binding.sparse_attn_ex(q, k, v, ident, bidx, w.C, kv_count=bcnt, scale=scale, want_lse=True,
+                                            out_dtype=torch.float32)
+        blocks = quality(o_b, lse_b)
+        del bidx, bcnt, o_s, o_b
+        out.append({"mode": "selection diagnostics (GPU, all queries)", "workload": workload, "density": s_, "K": K,
+                    "token_sparse_pddp": token, "block_sparse_contiguous": blocks})
+        log(args, f"[bench] diagnostics {workload} s={s_}: {out[-1]}")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
 
 def main():
     args = parse()
@@ -406,12 +607,20 @@ def main():
     if args.offload_layers > 0:
         print(json.dumps(measure_offload(args, args.workload, args.offload_layers, max(2, args.steps))), flush=True)
         return
+    if args.diagnostics:
+        for wl in ("tiny", "small", "large", "long", "asset3d"):
+            for line in measure_diagnostics(args, wl):
+                print(json.dumps(line), flush=True)
+        return
     if args.all_workloads:
-        # one JSON line per (workload, density); no CPU baseline
+        # one JSON line per (workload, density), then the measured schedule of
+        # every workload; no CPU baseline
         args.no_cpu_baseline = True
         for wl, dens in ALL_CONFIGS:
             out = measure(args, wl, dens, args.steps, args.warmup)
             print(json.dumps(out), flush=True)
+        for wl in ("tiny", "small", "large", "long", "asset3d"):
+            print(json.dumps({"mode": "measured schedule", **measure_schedule(args, wl)}), flush=True)
         return
     out = measure(args, args.workload, args.density, args.steps, args.warmup)
     print(json.dumps(out), flush=True)
