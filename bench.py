@@ -21,7 +21,8 @@ line each, with the anchor-path cost and the 50-step schedule with an anchor
 every 10 steps by formula), then runs every workload's step schedule on
 drifted inputs (the long workload: 50 steps, an anchor every 10).
 --diagnostics scores the token and block selections of every workload by
-attention recall and relative L1 error of the output, on the GPU.
+attention recall and relative L1 error of the output, on the GPU, and runs
+k-means grouping with its alignment inflation (mcs_kmeans).
 """
 from __future__ import annotations
 
@@ -589,8 +590,41 @@ def measure_diagnostics(args, workload: str) -> list:
         out.append({"mode": "selection diagnostics (GPU, all queries)", "workload": workload, "density": s_, "K": K,
                     "token_sparse_pddp": token, "block_sparse_contiguous": blocks})
         log(args, f"[bench] diagnostics {workload} s={s_}: {out[-1]}")
+    out.append(measure_kmeans(args, workload, q, k))
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    return out
+
+
+def measure_kmeans(args, workload: str, q, k, rounds: int = 20) -> dict:
+    """k-means grouping of head 0 on the GPU (mcs_kmeans): ceil(N/C) query
+    clusters and ceil(N/64) key clusters, Lloyd rounds from distinct seeded
+    rows (the same rows the CPU diagnostics start from), and the alignment
+    inflation of padding them to whole tiles."""
+    import torch
+
+    from token_sparse_attention_amd import binding, synth
+    w = synth.WORKLOADS[workload]
+    N = w.N
+    G = -(-N // w.C)
+    rng = np.random.default_rng(7000 + 100 * w.cfg_id + 0)
+    qi, ki = rng.choice(N, G, replace=False), rng.choice(N, -(-N // 64), replace=False)
+    res = {}
+    for name, x, idx, tile in (("queries", q[0, 0], qi, w.C), ("keys", k[0, 0], ki, 64)):
+        init = x[torch.from_numpy(idx).to(x.device)].float().contiguous()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _, _, inertia, sizes = binding.kmeans(x.contiguous(), init, rounds)
+        e1.record()
+        torch.cuda.synchronize()
+        sz = sizes.cpu().numpy()
+        sz = sz[sz > 0]
+        res[name] = {"clusters": int(idx.size), "empty": int(idx.size - sz.size), "min_size": int(sz.min()),
+                     "max_size": int(sz.max()), "inflation": round(float((-(-sz // tile) * tile).sum() / sz.sum()), 4),
+                     "final_inertia": round(float(inertia[-1].item()), 2), "ms": round(e0.elapsed_time(e1), 2)}
+    out = {"mode": "k-means grouping (GPU, head 0)", "workload": workload, "rounds": rounds, **res,
+           "inflation_blocks": round(res["queries"]["inflation"] * res["keys"]["inflation"], 4)}
+    log(args, f"[bench] k-means {workload}: {out}")
     return out
 
 

@@ -296,6 +296,28 @@ MCS_API mcs_status mcs_query_quality(const float* lse_dense, const float* lse_sp
 MCS_API mcs_status mcs_row_sums(const float* x, double* out, int64_t rows, int64_t n,
                         void* stream);
 
+/*
+ * Lloyd's k-means of one head's query or key rows, the grouping the pages set
+ * against exactly-C PDDP groups (ai.info, "Main Findings": k-means clusters of
+ * unequal size inflate the computed interactions once padded to whole tiles;
+ * wispaper.ai, "Token-level selection needs tile-aligned query groups").
+ * Each of `rounds` rounds: every row goes to the nearest centre (squared
+ * Euclidean distance in fp32, equal distances to the smaller centre id),
+ * inertia[r] = sum of the squared distances to those centres (fp64, fixed
+ * order), then every centre becomes the mean of its rows; a centre without
+ * rows keeps its place.
+ * In: x bf16 [n, D] (D = 64 or 128), init float32 [k, D] (initial centres;
+ * 1 <= k <= n).  Out: labels int32 [n] (the last round's assignment),
+ * centers float32 [k, D] (after the last update), inertia float64 [rounds],
+ * sizes int32 [k] (rows per centre in the last round).  The alignment
+ * inflation of tile T is sum_c ceil(sizes[c]/T)*T / n.
+ * ws: device workspace of mcs_kmeans_workspace(n, k) bytes.
+ */
+MCS_API mcs_status mcs_kmeans(const uint16_t* x, const float* init, int32_t n, int32_t D, int32_t k,
+                      int32_t rounds, int32_t* labels, float* centers, double* inertia,
+                      int32_t* sizes, void* ws, size_t ws_bytes, void* stream);
+MCS_API size_t mcs_kmeans_workspace(int32_t n, int32_t k);
+
 /* Static description of a status code. */
 MCS_API const char* mcs_status_string(mcs_status s);
 

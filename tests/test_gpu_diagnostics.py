@@ -153,3 +153,61 @@ def test_query_quality_and_row_sums(mcs):
     x = torch.from_numpy(np.random.default_rng(64).standard_normal((3, 100003)).astype(np.float32)).cuda()
     np.testing.assert_allclose(mcs.row_sums(x).cpu().numpy(), x.cpu().numpy().astype(np.float64).sum(axis=1),
                                rtol=1e-12)
+
+
+def test_kmeans_planted_clusters_exact(mcs):
+    # well-separated clusters of unequal sizes, centres started on one member
+    # each: labels, sizes and centres follow the oracle exactly (up to fp32)
+    rng = np.random.default_rng(71)
+    k, D = 12, 64
+    sizes = rng.integers(5, 90, size=k)
+    label = np.repeat(np.arange(k), sizes)
+    centres = 30.0 * rng.standard_normal((k, D))
+    x = synth.to_bf16_bits((centres[label] + 0.2 * rng.standard_normal((label.size, D))).astype(np.float32))
+    xf = synth.to_f64(x)
+    init = xf[np.cumsum(sizes) - 1].astype(np.float32)          # the last member of every cluster
+    ref_lab, ref_c, ref_in = dg.kmeans(xf, init.astype(np.float64), 4)
+    lab, c, inertia, sz = mcs.kmeans(to_dev_bf16(x), torch.from_numpy(init).cuda(), 4)
+    np.testing.assert_array_equal(lab.cpu().numpy(), ref_lab)
+    np.testing.assert_array_equal(sz.cpu().numpy(), np.bincount(ref_lab, minlength=k))
+    np.testing.assert_allclose(c.cpu().numpy(), ref_c, rtol=0, atol=1e-4)
+    np.testing.assert_allclose(inertia.cpu().numpy(), ref_in, rtol=1e-5)
+
+
+@pytest.mark.parametrize("name,N,clusters", [("small", 4096, 32), ("asset3d", 3000, 47)])
+def test_kmeans_workload_head_matches_oracle(mcs, name, N, clusters):
+    w = synth.WORKLOADS[name]
+    x = np.ascontiguousarray(synth.generate(name, heads=[(0, 0)])["q"][0, 0, :N])
+    xf = synth.to_f64(x)
+    rng = np.random.default_rng(72)
+    init = xf[rng.choice(N, clusters, replace=False)]
+    rounds = 10
+    ref_lab, ref_c, ref_in = dg.kmeans(xf, init, rounds)
+    lab, c, inertia, sz = mcs.kmeans(to_dev_bf16(x), torch.from_numpy(init.astype(np.float32)).cuda(), rounds)
+    lab, sz = lab.cpu().numpy(), sz.cpu().numpy()
+    # fp32 distances can settle a near-tie the other way and move a centre by
+    # a little: the inertia stays within 1e-4 and almost every label agrees
+    np.testing.assert_allclose(inertia.cpu().numpy(), ref_in, rtol=1e-4)
+    assert (lab == ref_lab).mean() >= 0.995, (lab != ref_lab).sum()
+    np.testing.assert_array_equal(sz, np.bincount(lab, minlength=clusters))
+    f_gpu = dg.alignment_inflation(sz[sz > 0], w.C)
+    f_ref = dg.alignment_inflation(np.bincount(ref_lab)[np.bincount(ref_lab) > 0], w.C)
+    assert abs(f_gpu - f_ref) <= 0.01 * f_ref, (f_gpu, f_ref)
+
+
+def test_kmeans_empty_cluster_keeps_its_centre(mcs):
+    # two identical initial centres: in the first round the second wins no
+    # point (ties go to the smaller id) and stays where it started; later
+    # rounds follow the oracle (the first centre moves away, so the second
+    # then wins the point it sits on)
+    rng = np.random.default_rng(73)
+    x = synth.to_bf16_bits(rng.standard_normal((300, 128)).astype(np.float32))
+    xf = synth.to_f64(x)
+    init = np.stack([xf[0], xf[0], xf[1]]).astype(np.float32)
+    lab, c, _, sz = mcs.kmeans(to_dev_bf16(x), torch.from_numpy(init).cuda(), 1)
+    assert sz.cpu().numpy()[1] == 0 and (lab.cpu().numpy() != 1).all()
+    np.testing.assert_array_equal(c.cpu().numpy()[1], init[1])
+    ref_lab, ref_c, _ = dg.kmeans(xf, init.astype(np.float64), 3)
+    lab, c, _, sz = mcs.kmeans(to_dev_bf16(x), torch.from_numpy(init).cuda(), 3)
+    np.testing.assert_array_equal(lab.cpu().numpy(), ref_lab)
+    np.testing.assert_allclose(c.cpu().numpy(), ref_c, rtol=0, atol=1e-4)

@@ -48,6 +48,8 @@ _SIGS = {
     "mcs_select_blocks_workspace": ([Dims], _SZ),
     "mcs_query_quality": ([_P, _P, _P, _P, _P, _P, _P, Dims, _P], _I32),
     "mcs_row_sums": ([_P, _P, _I64, _I64, _P], _I32),
+    "mcs_kmeans": ([_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "mcs_kmeans_workspace": ([_I32, _I32], _SZ),
     "mcs_select": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
     "mcs_select_two_pass": ([_P, _P, _P, _P, _P, Dims, _I32, _I32, _F, _P, _SZ, _P], _I32),
     "mcs_select_workspace": ([Dims, _I32, _I32], _SZ),
@@ -260,6 +262,25 @@ def row_sums(x):
     out = torch.empty(x.shape[0], dtype=torch.float64, device=x.device)
     _check(_lib.mcs_row_sums(_ptr(x), _ptr(out), x.shape[0], x.shape[1], _stream(x)))
     return out
+
+
+def kmeans(x, init, rounds):
+    """mcs_kmeans: Lloyd's k-means of the bf16 rows x [n, D] from the float32
+    centres init [k, D] -> (labels [n], centers [k, D], inertia [rounds] fp64, sizes [k])."""
+    _need(x, "x", torch.bfloat16, 2)
+    n, D = x.shape
+    _need(init, "init", torch.float32, 2)
+    k = init.shape[0]
+    if init.shape[1] != D or init.device != x.device:
+        raise ValueError(f"init must be [k, {D}] on {x.device}")
+    labels = torch.empty(n, dtype=torch.int32, device=x.device)
+    centers = torch.empty((k, D), dtype=torch.float32, device=x.device)
+    inertia = torch.empty(rounds, dtype=torch.float64, device=x.device)
+    sizes = torch.empty(k, dtype=torch.int32, device=x.device)
+    ws = torch.empty(max(int(_lib.mcs_kmeans_workspace(n, k)), 16), dtype=torch.uint8, device=x.device)
+    _check(_lib.mcs_kmeans(_ptr(x), _ptr(init), n, D, k, rounds, _ptr(labels), _ptr(centers), _ptr(inertia),
+                           _ptr(sizes), _ptr(ws), ws.numel(), _stream(x)))
+    return labels, centers, inertia, sizes
 
 
 def residual_update(o_dense, o_sparse, out=None):

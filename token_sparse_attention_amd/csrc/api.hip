@@ -400,6 +400,35 @@ mcs_status mcs_row_sums(const float* x, double* out, int64_t rows, int64_t n, vo
   return launched(fn, mcs::run_row_sums(x, out, rows, n, (hipStream_t)stream));
 }
 
+size_t mcs_kmeans_workspace(int32_t n, int32_t k) {
+  if (n < 1 || k < 1) return 0;
+  return mcs::kmeans_ws_bytes(n, k);
+}
+
+mcs_status mcs_kmeans(const uint16_t* x, const float* init, int32_t n, int32_t D, int32_t k, int32_t rounds,
+                      int32_t* labels, float* centers, double* inertia, int32_t* sizes, void* ws,
+                      size_t ws_bytes, void* stream) {
+  const char* fn = "mcs_kmeans";
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(init);
+  REQUIRE_PTR(labels);
+  REQUIRE_PTR(centers);
+  REQUIRE_PTR(inertia);
+  REQUIRE_PTR(sizes);
+  if (D != 64 && D != 128) return fail(MCS_E_HEAD_DIM, "%s: D must be 64 or 128 (got %d)", fn, D);
+  if (n < 1 || (int64_t)n * D > INT32_MAX)
+    return fail(MCS_E_SHAPE, "%s: n must be >= 1 with n*D < 2^31 (got n = %d)", fn, n);
+  if (k < 1 || k > n) return fail(MCS_E_ARG, "%s: k must be in [1, n=%d] (got %d)", fn, n, k);
+  if (rounds < 1 || rounds > 10000) return fail(MCS_E_ARG, "%s: rounds must be in [1, 10000] (got %d)", fn, rounds);
+  const size_t need = mcs::kmeans_ws_bytes(n, k);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MCS_E_WORKSPACE, "%s: workspace of %zu bytes given, at least %zu needed", fn,
+                ws == nullptr ? (size_t)0 : ws_bytes, need);
+  if (!aligned16(ws)) return fail(MCS_E_ALIGN, "%s: ws is not 16-byte aligned", fn);
+  return launched(fn, mcs::run_kmeans(x, init, n, D, k, rounds, labels, centers, inertia, sizes, ws,
+                                      (hipStream_t)stream));
+}
+
 const char* mcs_status_string(mcs_status s) {
   switch (s) {
     case MCS_OK: return "ok";

@@ -43,6 +43,11 @@ hipError_t run_query_quality(const float* lse_d, const float* lse_s, const float
                              float* recall, float* l1, float* l1ref, int64_t rows, int D, hipStream_t s);
 hipError_t run_row_sums(const float* x, double* out, int64_t rows, int64_t n, hipStream_t s);
 
+// Lloyd's k-means of n rows of D bf16 values (kmeans.hip).
+size_t kmeans_ws_bytes(int n, int k);
+hipError_t run_kmeans(const uint16_t* x, const float* init, int n, int D, int k, int rounds, int32_t* labels,
+                      float* centers, double* inertia, int32_t* sizes, void* ws, hipStream_t s);
+
 // Median-split PDDP.
 struct GroupPlan {
   int levels;        // number of split levels
