@@ -7,6 +7,7 @@ validation, which the library rejects before touching HIP.
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -204,3 +205,27 @@ def test_header_is_plain_c_and_links(lib, tmp_path):
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(root, "include"),
                     str(src), "-L", lib_dir, "-lmcs", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def test_validation_under_address_and_ub_sanitizers(tmp_path):
+    """The C-ABI layer (api.hip) built with ASan and UBSan on the host code and
+    linked with host stand-ins for the launchers (tests/abi_sanitize): every
+    entry point's checks and accepting path run clean on a machine without a
+    GPU.  Sanitizers apply to the host code only (each -fsanitize= follows
+    -Xarch_host)."""
+    import shlex
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    here = os.path.join(ROOT, "tests", "abi_sanitize")
+    exe = str(tmp_path / "abi_sanitize")
+    san = shlex.split("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                      "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer")
+    cmd = [hipcc, "-O1", "-g", "-std=c++17", "--offload-arch=gfx950", *san, "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "token_sparse_attention_amd", "csrc", "api.hip"), os.path.join(here, "stubs.cpp"),
+           os.path.join(here, "driver.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0 and "sanitize ok" in r.stdout, (r.stdout[-2000:], r.stderr[-4000:])
