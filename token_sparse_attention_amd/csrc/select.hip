@@ -11,9 +11,9 @@
 // (gathered by perm) stay in registers as MFMA A fragments; all N keys stream
 // through LDS in tiles of 64 (double buffered).  S = Q K^T on MFMA leaves one
 // key per lane column, so each lane sums exp2(s*scale*log2e - lse_i*log2e)
-// over its 16 query rows, adds its partner lane's half, and the C/32 waves
-// combine through LDS in a fixed order.  One fp32 mass row of N values per
-// group goes to the workspace.  The fused form (aggregation and top-K in one
+// over its 16 query rows; the two half-waves' sums and the C/32 waves combine
+// through LDS in a fixed order, one wave per tile in turn.  One fp32 mass row
+// of N values per group goes to the workspace.  The fused form (aggregation and top-K in one
 // kernel, as the ai.info page describes the second pass) also histograms the
 // first digit of each finished mass during the sweep, then selects the K ids
 // from the row it has just written, in the same workgroup: two more digit
@@ -65,11 +65,12 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   constexpr int INSTR = TILE_BYTES / 1024;  // 1 KiB DMA instructions per tile
   constexpr int IPW = INSTR / NW;
   constexpr int ROWS_PER_INSTR = 64 / CH;
-  constexpr int RED_KEYS = MKT / NW;        // keys each wave reduces per tile
-  static_assert(INSTR % NW == 0 && RED_KEYS <= 64, "tile split");
+  static_assert(INSTR % NW == 0 && MKT == 64 && (NW & (NW - 1)) == 0, "tile split");
 
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][MKT * D];
-  __shared__ float red[2][NW][MKT];
+  // per tile buffer, wave and 32-key block: the 16-row partial sums of the
+  // lanes, lane L holding key L % 32 of the block
+  __shared__ float red[2][NW][2][64];
   // fused top-K: histogram of the first 9-bit digit of the keys, filled as
   // the masses are completed
   constexpr int H1 = 512;
@@ -128,30 +129,33 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   for (int ks = 0; ks < KSTEPS; ++ks)
     koff[ks] = (uint32_t)(lq * ROWB + (((2 * ks + hh) ^ swz<D>(lq)) << 4));
 
-  // mass of one 32-key block: sum over this lane's 16 query rows, then the
-  // partner lane's 16; four partial sums keep the add chains short
+  // partial mass of one 32-key block: the sum over this lane's 16 query rows
+  // (the partner lane L ^ 32 holds the other 16); four partial sums keep the
+  // add chains short
   auto block_mass = [&](const f32x16_t& acc) {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    auto term = [&](int e) { return fast_exp2(fmaf(acc[e], p.sl2, -lse2[e])); };
+    float s0 = term(0), s1 = term(1), s2 = term(2), s3 = term(3);
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      s0 += fast_exp2(fmaf(acc[e], p.sl2, -lse2[e]));
-      s1 += fast_exp2(fmaf(acc[e + 1], p.sl2, -lse2[e + 1]));
-      s2 += fast_exp2(fmaf(acc[e + 2], p.sl2, -lse2[e + 2]));
-      s3 += fast_exp2(fmaf(acc[e + 3], p.sl2, -lse2[e + 3]));
+    for (int e = 4; e < 16; e += 4) {
+      s0 += term(e);
+      s1 += term(e + 1);
+      s2 += term(e + 2);
+      s3 += term(e + 3);
     }
-    return halves_sum((s0 + s1) + (s2 + s3));
+    return (s0 + s1) + (s2 + s3);
   };
 
   float* __restrict__ mrow = p.mass + ((size_t)hl * p.G + g) * p.N;
-  // the waves' partial masses of tile t, summed in wave order
+  // the mass of key `lane` of tile t: per wave, the two half-wave partial
+  // sums added, then the waves summed in order.  Wave t % NW does it, so the
+  // work rotates over the SIMDs.
   auto store_tile = [&](int t) {
-    const int b = t & 1;
-    const int kk = w * RED_KEYS + lane;
-    const int key = t * MKT + kk;
-    if (lane < RED_KEYS && key < p.N) {
-      float s = red[b][0][kk];
+    const int b = t & 1, blk = lane >> 5, lk = lane & 31;
+    const int key = t * MKT + lane;
+    if (w == (t & (NW - 1)) && key < p.N) {
+      float s = red[b][0][blk][lk] + red[b][0][blk][32 + lk];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) s += red[b][ww][kk];
+      for (int ww = 1; ww < NW; ++ww) s += red[b][ww][blk][lk] + red[b][ww][blk][32 + lk];
       mrow[key] = s;
       if (FUSED) atomicAdd(&h1[mass_key31(__float_as_uint(s)) >> 22], 1u);
     }
@@ -177,12 +181,8 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
       acc0 = mfma32x32x16(qf[ks], as_bf16x8(*reinterpret_cast<const u32x4_t*>(kt + koff[ks])), acc0);
       acc1 = mfma32x32x16(qf[ks], as_bf16x8(*reinterpret_cast<const u32x4_t*>(kt + 32 * ROWB + koff[ks])), acc1);
     }
-    const float m0 = block_mass(acc0);
-    const float m1 = block_mass(acc1);
-    if (hh == 0) {
-      red[BUF][w][lq] = m0;
-      red[BUF][w][32 + lq] = m1;
-    }
+    red[BUF][w][0][lane] = block_mass(acc0);
+    red[BUF][w][1][lane] = block_mass(acc1);
   };
   issue(0, 0);
   int t = 0;
