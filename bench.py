@@ -144,7 +144,7 @@ def measured_traffic(workload: str, kernel_prefix: str):
     if d.get("source_hash") != pmc.source_hash():
         return None
     for name, v in d["kernels"].items():
-        if name.startswith(kernel_prefix):
+        if name.startswith(kernel_prefix) and not name.endswith(pmc.BSA_SUFFIX):
             return v["traffic_bytes"]
     return None
 
@@ -161,7 +161,7 @@ def measured_util(workload: str, kernel_prefix: str):
     if d.get("source_hash") != pmc.source_hash():
         return None
     for name, v in d["kernels"].items():
-        if name.startswith(kernel_prefix):
+        if name.startswith(kernel_prefix) and not name.endswith(pmc.BSA_SUFFIX):
             return v
     return None
 

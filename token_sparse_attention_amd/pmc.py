@@ -3,6 +3,7 @@
     python -m token_sparse_attention_amd.pmc FETCH_DIR WRITE_DIR OUT.json [--workload large]
     python -m token_sparse_attention_amd.pmc --util UTIL_DIR OUT.json
     python -m token_sparse_attention_amd.pmc --l2 L2_DIR OUT.json
+    python -m token_sparse_attention_amd.pmc --trace TRACE_DIR OUT.json
 
 FETCH_DIR and WRITE_DIR are the output directories of two runs of
 
@@ -35,6 +36,16 @@ per wave), and the VALU (MFMA excluded) and LDS instructions per MFMA.
 
 per kernel: L2 hits and misses per dispatch and the hit rate (a miss is a
 128-byte line requested from the fabric: MALL or HBM).
+
+--trace summarises the kernel_trace.csv of one
+
+    rocprofv3 --kernel-trace --stats -d TRACE_DIR -o bench --output-format csv -- python3 bench.py ...
+
+per kernel: calls, mean / min / max dispatch time and share of the GPU time.
+
+In all four, attention dispatches issued after the first block_means_kernel
+(bench.py's block-sparse comparison, the same kernel over whole key blocks)
+are reported under the kernel's name with " [block-sparse]" appended.
 """
 from __future__ import annotations
 
@@ -68,15 +79,33 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+BSA_MARK = "block_means_kernel"   # bench.py's block-sparse comparison starts with it
+BSA_SUFFIX = " [block-sparse]"
+
+
+def _rows(directory: str, kind: str = "counter_collection"):
+    """Counter rows of a run with the short kernel name; attention dispatches
+    issued after the block-sparse comparison began (the same kernel over the
+    blocks' tokens) are named apart, so the token-sparse figures hold only the
+    token-sparse launches."""
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", f"*{kind}.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    names = [r["Kernel_Name"].split("(")[0].replace("void ", "").replace("mcs::", "") for r in rows]
+    marks = [int(r["Dispatch_Id"]) for r, n in zip(rows, names) if n.startswith(BSA_MARK)]
+    start = min(marks) if marks else None
+    for r, n in zip(rows, names):
+        if start is not None and n.startswith("attn_kernel") and int(r["Dispatch_Id"]) > start:
+            n += BSA_SUFFIX
+        yield n, r
+
+
 def _per_kernel(directory: str, counter: str) -> dict:
     vals = defaultdict(lambda: defaultdict(float))
-    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                if r["Counter_Name"] != counter:
-                    continue
-                name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("mcs::", "")
-                vals[name][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    for name, r in _rows(directory):
+        if r["Counter_Name"] == counter:
+            vals[name][r["Dispatch_Id"]] += float(r["Counter_Value"])
     return {k: sum(d.values()) / len(d) for k, d in vals.items() if d}
 
 
@@ -106,13 +135,10 @@ N_SIMD = 256 * 4
 def utilisation(util_dir: str) -> dict:
     rows = defaultdict(lambda: defaultdict(float))
     times = defaultdict(dict)
-    for f in glob.glob(os.path.join(util_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("mcs::", "")
-                d = r["Dispatch_Id"]
-                rows[(name, d)][r["Counter_Name"]] += float(r["Counter_Value"])
-                times[(name, d)] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    for name, r in _rows(util_dir):
+        d = r["Dispatch_Id"]
+        rows[(name, d)][r["Counter_Name"]] += float(r["Counter_Value"])
+        times[(name, d)] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
     acc = defaultdict(lambda: defaultdict(float))
     for (name, d), c in rows.items():
         t0, t1 = times[(name, d)]
@@ -152,6 +178,19 @@ def l2(l2_dir: str) -> dict:
     return {"source_hash": source_hash(), "kernels": out}
 
 
+def trace(trace_dir: str) -> dict:
+    """Per kernel: calls, mean / min / max dispatch time (ms) and share of the
+    GPU time, from a --kernel-trace run (block-sparse launches apart)."""
+    ms = defaultdict(list)
+    for name, r in _rows(trace_dir, "kernel_trace"):
+        ms[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
+    total = sum(sum(v) for v in ms.values())
+    out = {k: {"calls": len(v), "mean_ms": sum(v) / len(v), "min_ms": min(v), "max_ms": max(v),
+               "share": sum(v) / total} for k, v in ms.items()}
+    return {"source_hash": source_hash(),
+            "kernels": dict(sorted(out.items(), key=lambda kv: -kv[1]["share"]))}
+
+
 def main(argv):
     if argv and argv[0] == "--l2":
         out = l2(argv[1])
@@ -160,6 +199,14 @@ def main(argv):
         for k, v in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["misses"]):
             print(f"{k:48s} hit rate {100 * (v['hit_rate'] or 0):5.1f}%  misses {v['misses']:.3e}"
                   f"  ({v['miss_bytes'] / 1e9:.2f} GB of lines)")
+        return 0
+    if argv and argv[0] == "--trace":
+        out = trace(argv[1])
+        with open(argv[2], "w") as f:
+            json.dump(out, f, indent=1)
+        for k, v in out["kernels"].items():
+            print(f"| `{k}` | {v['calls']} | {v['mean_ms']:.3f} | {v['min_ms']:.3f} | {v['max_ms']:.3f}"
+                  f" | {100 * v['share']:.2f} |")
         return 0
     if argv and argv[0] == "--util":
         out = utilisation(argv[1])
