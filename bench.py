@@ -133,15 +133,15 @@ def cpu_model() -> str:
 
 
 def measured_traffic(workload: str, kernel_prefix: str):
-    """HBM bytes per launch from the committed counter summary, if it still
-    describes the current kernel sources (else None)."""
+    """HBM bytes per launch of an attention kernel from the committed counter
+    summary, if it still describes the current attention sources (else None)."""
     from token_sparse_attention_amd import pmc
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_hash") != pmc.source_hash():
+    if d.get("attn_source_hash") != pmc.source_hash(pmc.ATTN_SOURCES):
         return None
     for name, v in d["kernels"].items():
         if name.startswith(kernel_prefix) and not name.endswith(pmc.BSA_SUFFIX):
@@ -158,7 +158,7 @@ def measured_util(workload: str, kernel_prefix: str):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_hash") != pmc.source_hash():
+    if d.get("attn_source_hash") != pmc.source_hash(pmc.ATTN_SOURCES):
         return None
     for name, v in d["kernels"].items():
         if name.startswith(kernel_prefix) and not name.endswith(pmc.BSA_SUFFIX):

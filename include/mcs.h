@@ -222,9 +222,11 @@ MCS_API mcs_status mcs_topk(const float* scores, int32_t* idx, int64_t rows, int
  * by Lanczos with full reorthogonalisation (the Krylov form of power
  * iteration: the same matrix-vector products, but it converges where power
  * steps stall on nearly equal leading eigenvalues), started from the
- * covariance column of largest diagonal, for lanczos_steps steps
- * (<= 0 selects the default, 32; at most 64).  Covariance, Lanczos and
- * projections are fp32; the small tridiagonal eigenproblem is fp64.
+ * covariance column of largest diagonal, for at most lanczos_steps steps
+ * (<= 0 selects the default, 32; at most 64); when that is more than 16, the
+ * iteration ends after 16 steps if the top Ritz pair's residual is below
+ * 1e-6 of its Ritz value.  Covariance, Lanczos and projections are fp32; the
+ * small tridiagonal eigenproblem is fp64.
  * In: q bf16 [B,H,N,D].  Out: perm int32 [B,H,N].  ws: device workspace of at
  * least mcs_group_workspace(d, C) bytes.
  */

@@ -25,8 +25,10 @@
 //                  sum(x) and sum(x x^T) on bf16 MFMA with fp32 accumulation;
 //   pddp_direction one workgroup per node: moments (summed partials, or
 //                  computed directly for small nodes) -> covariance ->
-//                  Lanczos -> top eigenvector v of the covariance with its
-//                  largest-magnitude component positive, and mu.v;
+//                  Lanczos (up to 32 steps, ending after 16 when the Ritz
+//                  residual has converged) -> top eigenvector v of the
+//                  covariance with its largest-magnitude component
+//                  positive, and mu.v;
 //   pddp_project   p_i = x_i.v - mu.v for every query of the node (fp32);
 //   pddp_split     radix select of the rank-(C*floor(g/2)) projection and a
 //                  stable partition of the node's perm range.
@@ -41,6 +43,12 @@ constexpr int CHUNK_M = 2048;    // queries per partial-moment chunk
 constexpr int MSTEP = 64;        // queries staged in LDS per MFMA step
 constexpr int DEFAULT_STEPS = 32;  // Lanczos steps (Krylov dimension) by default
 constexpr int KRYLOV_MAX = 64;     // most Lanczos steps; the basis fills the moment staging LDS
+// One convergence test of the Lanczos direction, after STOP_AT steps: the
+// iteration ends there when the Ritz residual is below STOP_TOL times the
+// Ritz value (a test costs about three steps, so one well-placed test saves
+// more than frequent ones).
+constexpr int STOP_AT = 16;
+constexpr double STOP_TOL = 1e-6;
 
 __device__ __forceinline__ int swz_st(int d) { return (d >> 1) & 7; }
 
@@ -204,8 +212,12 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   __shared__ float sred[MSTEP / 4][D];
   __shared__ float part[2][RB][D];
   __shared__ float mu[D];
-  __shared__ float tri[2][KRYLOV_MAX];           // alpha, beta of the Lanczos recurrence
-  __shared__ double tri_d[KRYLOV_MAX], tri_x[KRYLOV_MAX];
+  // per wave: alpha, beta of the Lanczos recurrence and the tridiagonal
+  // solve's pivots and vector (every wave holds the same recurrence and runs
+  // the same solve, so all take the same stop decision without a barrier)
+  constexpr int NWAVE = PD_NT / 64;
+  __shared__ float tri[NWAVE][2][KRYLOV_MAX];
+  __shared__ double tri_d[NWAVE][KRYLOV_MAX], tri_x[NWAVE][KRYLOV_MAX];
   __shared__ int ish[2];
   constexpr int NV = D / 64;                     // vector components per lane
   static_assert(sizeof(MomentLds<D>) >= sizeof(float) * KRYLOV_MAX * D, "basis must fit the staging LDS");
@@ -411,6 +423,100 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     for (int k = 0; k < NV; ++k) wv[k] -= dw[k];
     after = before - hsq;
   };
+  // The top eigenpair (theta, s) of the mm x mm tridiagonal T =
+  // tridiag(beta, alpha, beta) held in this wave's arrays: s goes to tx,
+  // theta (from above, to the multisection's resolution) is returned.  The
+  // recurrences are sequential in i and run on wave-uniform values: alpha_i
+  // and beta_i sit in lane i and are broadcast with readlane, reciprocals are
+  // v_rcp_f64 refined by one Newton step (relative error ~1e-14), and the
+  // pivots of the inverse iteration are formed once for both of its sweeps.
+  float* const ta = tri[w][0];
+  float* const tb = tri[w][1];
+  double* const td = tri_d[w];
+  double* const tx = tri_x[w];
+  auto rcp64 = [](double d) {
+    const double r = __builtin_amdgcn_rcp(d);
+    return fma(r, fma(-d, r, 1.0), r);
+  };
+  auto top_pair = [&](int mm) -> double {
+    const float al = lane < mm ? ta[lane] : 0.f;
+    const float bl = lane < mm ? tb[lane] : 0.f;
+    auto a_at = [&](int i) { return (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), i)); };
+    auto b_at = [&](int i) { return (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl), i)); };
+    // Gershgorin interval, then multisection on Sturm counts: lane l counts
+    // the eigenvalues below lo + (hi - lo) (l + 1) / 65, and the interval
+    // shrinks to the two shifts around the largest eigenvalue.
+    double lo = INFINITY, hi = -INFINITY;
+    for (int i = 0; i < mm; ++i) {
+      const double r = (i > 0 ? fabs(b_at(i - 1)) : 0.0) + (i + 1 < mm ? fabs(b_at(i)) : 0.0);
+      lo = fmin(lo, a_at(i) - r);
+      hi = fmax(hi, a_at(i) + r);
+    }
+    if (mm > 1 && hi > lo) {
+      for (int round = 0; round < 5; ++round) {
+        const double x = lo + (hi - lo) * (double)(lane + 1) / 65.0;
+        int cnt = 0;
+        double d = 1.0;
+        for (int i = 0; i < mm; ++i) {
+          const double bb = i > 0 ? b_at(i - 1) : 0.0;
+          d = (a_at(i) - x) - (i > 0 ? bb * bb * rcp64(d) : 0.0);
+          if (d == 0.0) d = -1e-300;
+          cnt += d < 0.0;
+        }
+        const uint64_t above = __builtin_amdgcn_ballot_w64(cnt >= mm);
+        if (above == 0) {
+          lo = lo + (hi - lo) * 64.0 / 65.0;
+        } else {
+          const int f = __builtin_ctzll(above);
+          const double nhi = lo + (hi - lo) * (double)(f + 1) / 65.0;
+          const double nlo = f > 0 ? lo + (hi - lo) * (double)f / 65.0 : lo;
+          lo = nlo;
+          hi = nhi;
+        }
+      }
+    }
+    if (mm == 1) {
+      if (lane == 0) tx[0] = 1.0;
+      return a_at(0);
+    }
+    // Inverse iteration with the shift sigma just above the largest
+    // eigenvalue: sigma I - T is positive definite there, so its LU
+    // factorisation needs no pivoting.  td holds the reciprocal pivots 1/d_i;
+    // two sweeps from the all-ones vector.
+    const double sigma = hi + fmax(hi - lo, 1e-9 * fabs(hi)) + 1e-300;
+    {
+      double rprev = 0.0;
+      for (int i = 0; i < mm; ++i) {
+        const double bb = i > 0 ? b_at(i - 1) : 0.0;
+        const double dn = (sigma - a_at(i)) - (i > 0 ? bb * bb * rprev : 0.0);
+        rprev = rcp64(dn);
+        if (lane == 0) {
+          td[i] = rprev;
+          tx[i] = 1.0;
+        }
+      }
+    }
+    for (int iter = 0; iter < 2; ++iter) {
+      double yprev = 0.0;
+      for (int i = 0; i < mm; ++i) {       // forward: L y = x
+        const double yi = tx[i] + (i > 0 ? b_at(i - 1) * td[i - 1] * yprev : 0.0);
+        yprev = yi;
+        if (lane == 0) tx[i] = yi;
+      }
+      double xnext = 0.0, s2 = 0.0;
+      for (int i = mm - 1; i >= 0; --i) {  // back substitution: U x = y
+        const double bb = i + 1 < mm ? b_at(i) : 0.0;
+        const double xi = (tx[i] + bb * xnext) * td[i];
+        xnext = xi;
+        s2 += xi * xi;
+        if (lane == 0) tx[i] = xi;
+      }
+      const double inv = 1.0 / sqrt(s2);
+      for (int i = 0; i < mm; ++i)
+        if (lane == 0) tx[i] *= inv;
+    }
+    return hi;
+  };
   int m = 0;
   float bprev = 0.f;
   for (int j = 0; j < steps; ++j) {
@@ -450,7 +556,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
       a = fmaf(vj[k], v, a);
     }
     a = uniform_f(wave_sum(a));
-    if (w == 0 && lane == 0) tri[0][j] = a;
+    if (lane == 0) ta[j] = a;
     m = j + 1;
     if (j + 1 >= steps) break;
 #pragma unroll
@@ -472,7 +578,13 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     // Pythagorean norm is accurate to a few ulps
     if (invariant) break;
     const float bnew = sqrtf(n1), inv = 1.f / bnew;
-    if (w == 0 && lane == 0) tri[1][j] = bnew;
+    if (lane == 0) tb[j] = bnew;
+    // stop if the top Ritz pair of T (j + 1 steps) has converged: its
+    // residual |C y - theta y| is beta_j |s_last|
+    if (j + 1 == STOP_AT && j + 1 < steps) {
+      const double th = top_pair(j + 1);
+      if ((double)bnew * fabs(tx[j]) <= STOP_TOL * fabs(th)) break;
+    }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       vprev[k] = vj[k];
@@ -483,87 +595,16 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     bprev = bnew;
   }
   // From here on only wave 0 works (no further barriers): the top eigenpair
-  // of the m x m tridiagonal T = tridiag(beta, alpha, beta), then the Ritz
-  // vector.  All of the basis is visible: its last vector was written before
-  // the last step's barrier.
+  // of the m x m tridiagonal, then the Ritz vector.  All of the basis is
+  // visible: its last vector was written before the last step's barrier.
   if (w != 0) return;
-  double theta_hi;
-  {
-    // Gershgorin interval, then multisection on Sturm counts: lane l counts
-    // the eigenvalues below lo + (hi - lo) (l + 1) / 65, and the interval
-    // shrinks to the two shifts around the largest eigenvalue, 5 times.
-    double lo = INFINITY, hi = -INFINITY;
-    for (int i = 0; i < m; ++i) {
-      const double r = (i > 0 ? fabs((double)tri[1][i - 1]) : 0.0) + (i + 1 < m ? fabs((double)tri[1][i]) : 0.0);
-      lo = fmin(lo, (double)tri[0][i] - r);
-      hi = fmax(hi, (double)tri[0][i] + r);
-    }
-    if (m > 1 && hi > lo) {
-      for (int round = 0; round < 5; ++round) {
-        const double x = lo + (hi - lo) * (double)(lane + 1) / 65.0;
-        int cnt = 0;
-        double d = 1.0;
-        for (int i = 0; i < m; ++i) {
-          const double bb = i > 0 ? (double)tri[1][i - 1] : 0.0;
-          d = ((double)tri[0][i] - x) - (i > 0 ? bb * bb / d : 0.0);
-          if (d == 0.0) d = -1e-300;
-          cnt += d < 0.0;
-        }
-        const uint64_t above = __builtin_amdgcn_ballot_w64(cnt >= m);
-        if (above == 0) {
-          lo = lo + (hi - lo) * 64.0 / 65.0;
-        } else {
-          const int f = __builtin_ctzll(above);
-          const double nhi = lo + (hi - lo) * (double)(f + 1) / 65.0;
-          const double nlo = f > 0 ? lo + (hi - lo) * (double)f / 65.0 : lo;
-          lo = nlo;
-          hi = nhi;
-        }
-      }
-    }
-    theta_hi = hi + fmax(hi - lo, 1e-9 * fabs(hi)) + 1e-300;
-  }
-  // Inverse iteration with the shift sigma just above the largest eigenvalue:
-  // sigma I - T is positive definite there, so its LU recurrence needs no
-  // pivoting.  Two steps from the all-ones vector.  s goes through LDS.
-  if (m == 1) {
-    if (lane == 0) tri_x[0] = 1.0;
-  } else {
-    const double sigma = theta_hi;
-    for (int i = 0; i < m; ++i)
-      if (lane == 0) tri_x[i] = 1.0;
-    for (int iter = 0; iter < 2; ++iter) {
-      double d = 0.0, yprev = 0.0;
-      for (int i = 0; i < m; ++i) {        // forward: pivots d_i and y
-        const double bb = i > 0 ? (double)tri[1][i - 1] : 0.0;
-        const double dn = (sigma - (double)tri[0][i]) - (i > 0 ? bb * bb / d : 0.0);
-        const double yi = tri_x[i] + (i > 0 ? bb / d * yprev : 0.0);
-        d = dn;
-        yprev = yi;
-        if (lane == 0) {
-          tri_d[i] = dn;
-          tri_x[i] = yi;
-        }
-      }
-      double xnext = 0.0, s2 = 0.0;
-      for (int i = m - 1; i >= 0; --i) {   // back substitution
-        const double bb = i + 1 < m ? (double)tri[1][i] : 0.0;
-        const double xi = (tri_x[i] + bb * xnext) / tri_d[i];
-        xnext = xi;
-        s2 += xi * xi;
-        if (lane == 0) tri_x[i] = xi;
-      }
-      const double inv = 1.0 / sqrt(s2);
-      for (int i = 0; i < m; ++i)
-        if (lane == 0) tri_x[i] *= inv;
-    }
-  }
+  top_pair(m);
   // Ritz vector y = sum_j s_j V_j, normalised
   float y[NV], s2 = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) y[k] = 0.f;
   for (int j = 0; j < m; ++j) {
-    const float sj = (float)tri_x[j];
+    const float sj = (float)tx[j];
 #pragma unroll
     for (int k = 0; k < NV; ++k) y[k] = fmaf(sj, Vb[j * D + lane + 64 * k], y[k]);
   }

@@ -68,11 +68,18 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def source_hash() -> str:
-    """Hash of the code of the HIP sources the counters describe (comments and
-    whitespace do not count, so editing a comment keeps the counters valid)."""
+# the files the attention kernels are built from
+ATTN_SOURCES = ("attn.hip", "mcs_common.h", "mcs_internal.h")
+
+
+def source_hash(files=None) -> str:
+    """Hash of the code of the HIP sources the counters describe, all of them
+    or the named files (comments and whitespace do not count, so editing a
+    comment keeps the counters valid)."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        if files is not None and os.path.basename(f) not in files:
+            continue
         with open(f, encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
             h.update(_code_only(fh.read()).encode())
@@ -125,7 +132,8 @@ def summarize(fetch_dir: str, write_dir: str, workload: str) -> dict:
         kernels[k] = {"fetch_kib_raw": fetch.get(k), "write_kib_raw": write.get(k),
                       "read_bytes": rd, "write_bytes": wr, "traffic_bytes": rd + wr}
     return {"workload": workload, "calibration_kernel": cal, "read_scale": f_read,
-            "write_scale": f_write, "source_hash": source_hash(), "kernels": kernels}
+            "write_scale": f_write, "source_hash": source_hash(),
+            "attn_source_hash": source_hash(ATTN_SOURCES), "kernels": kernels}
 
 
 N_XCD = 8
@@ -164,7 +172,8 @@ def utilisation(util_dir: str) -> dict:
         n = a.pop("n")
         out[name] = {k: v / n for k, v in a.items()}
         out[name]["dispatches"] = int(n)
-    return {"source_hash": source_hash(), "kernels": out}
+    return {"source_hash": source_hash(),
+            "attn_source_hash": source_hash(ATTN_SOURCES), "kernels": out}
 
 
 def l2(l2_dir: str) -> dict:
@@ -175,7 +184,8 @@ def l2(l2_dir: str) -> dict:
         tot = hits[k] + miss[k]
         out[k] = {"hits": hits[k], "misses": miss[k], "hit_rate": hits[k] / tot if tot else None,
                   "miss_bytes": 128.0 * miss[k]}
-    return {"source_hash": source_hash(), "kernels": out}
+    return {"source_hash": source_hash(),
+            "attn_source_hash": source_hash(ATTN_SOURCES), "kernels": out}
 
 
 def trace(trace_dir: str) -> dict:
@@ -187,7 +197,7 @@ def trace(trace_dir: str) -> dict:
     total = sum(sum(v) for v in ms.values())
     out = {k: {"calls": len(v), "mean_ms": sum(v) / len(v), "min_ms": min(v), "max_ms": max(v),
                "share": sum(v) / total} for k, v in ms.items()}
-    return {"source_hash": source_hash(),
+    return {"source_hash": source_hash(), "attn_source_hash": source_hash(ATTN_SOURCES),
             "kernels": dict(sorted(out.items(), key=lambda kv: -kv[1]["share"]))}
 
 
