@@ -55,6 +55,15 @@ def lib():
     lib.mcs_select_workspace.restype = SZ
     lib.mcs_select_workspace_all_heads.argtypes = [Dims, I32, I32]
     lib.mcs_select_workspace_all_heads.restype = SZ
+    lib.mcs_sparse_attn_ex.argtypes = [P, P, P, P, P, P, P, P, I32, P, Dims, I32, I32, F, P]
+    lib.mcs_select_blocks.argtypes = [P, P, P, P, P, Dims, I32, I32, F, P, SZ, P]
+    lib.mcs_select_blocks_workspace.argtypes = [Dims]
+    lib.mcs_select_blocks_workspace.restype = SZ
+    lib.mcs_query_quality.argtypes = [P, P, P, P, P, P, P, Dims, P]
+    lib.mcs_row_sums.argtypes = [P, P, I64, I64, P]
+    lib.mcs_kmeans.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P, P, SZ, P]
+    lib.mcs_kmeans_workspace.argtypes = [I32, I32]
+    lib.mcs_kmeans_workspace.restype = SZ
     lib.mcs_status_string.restype = ctypes.c_char_p
     lib.mcs_last_error.restype = ctypes.c_char_p
     return lib
@@ -165,6 +174,52 @@ def test_group_noalloc_validation(lib):
     assert lib.mcs_group_workspace(big, 128) > 64 << 20
     assert lib.mcs_group_noalloc(A, B_, big, 128, 0, None) == c["MCS_E_WORKSPACE"]
     assert b"scratch" in lib.mcs_last_error()
+
+
+def test_block_sparse_and_diagnostic_validation(lib):
+    c = _codes()
+    d = Dims(1, 2, 1000, 128)
+    W = 0x80000
+    # sparse attention with counts / LSE
+    ex = lambda **kw: [kw.get(k, v) for k, v in dict(q=A, k=B_, v=C_, perm=D_, idx=E_, cnt=None, res=None,
+                                                     o=0x60000, f32=0, lse=None).items()]
+    assert lib.mcs_sparse_attn_ex(*ex(res=0x70000, lse=0x90000), d, 128, 64, 0.1, None) == c["MCS_E_ARG"]
+    assert b"residual and lse" in lib.mcs_last_error()
+    assert lib.mcs_sparse_attn_ex(*ex(cnt=0x90004), d, 128, 64, 0.1, None) == c["MCS_E_ALIGN"]
+    assert lib.mcs_sparse_attn_ex(*ex(idx=None), d, 128, 64, 0.1, None) == c["MCS_E_NULL"]
+    assert lib.mcs_sparse_attn_ex(*ex(), d, 128, 1001, 0.1, None) == c["MCS_E_BUDGET"]
+    # block selection: K whole 64-key blocks, at most the head's block count
+    need = lib.mcs_select_blocks_workspace(d)
+    assert need == 2 * 16 * 128 * 4                       # fp32 mean key per block, ceil(1000 / 64) = 16
+    assert lib.mcs_select_blocks_workspace(Dims(1, 2, 1000, 96)) == 0
+    sb = lambda K, cnt=0x90000, ws=W, nb=need, dims=d: lib.mcs_select_blocks(A, B_, C_, D_, cnt, dims, 128, K, 0.1,
+                                                                             ws, nb, None)
+    for K in (0, 63, 100, 17 * 64):
+        assert sb(K) == c["MCS_E_BUDGET"], K
+    assert sb(128, cnt=None) == c["MCS_E_NULL"]
+    assert sb(128, nb=need - 1) == c["MCS_E_WORKSPACE"]
+    assert sb(128, ws=None) == c["MCS_E_WORKSPACE"]
+    assert sb(128, ws=W + 8) == c["MCS_E_ALIGN"]
+    big = Dims(1, 1, 4096 * 64 + 1, 64)                   # one key block more than the selector holds
+    assert sb(128, dims=big, nb=1 << 40) == c["MCS_E_SHAPE"]
+    # per-query recall and L1 terms; fixed-order row sums
+    assert lib.mcs_query_quality(A, None, C_, D_, E_, 0x60000, 0x70000, d, None) == c["MCS_E_NULL"]
+    assert lib.mcs_query_quality(A, B_, C_, D_, E_, 0x60000, 0x70000, Dims(1, 2, 1000, 96), None) == c["MCS_E_HEAD_DIM"]
+    assert lib.mcs_row_sums(A, B_, 0, 10, None) == c["MCS_E_SHAPE"]
+    assert lib.mcs_row_sums(A, B_, 3, 0, None) == c["MCS_E_SHAPE"]
+    assert lib.mcs_row_sums(None, B_, 3, 10, None) == c["MCS_E_NULL"]
+    # k-means
+    kws = lib.mcs_kmeans_workspace(1000, 8)
+    assert kws >= (1000 + 8) * 4
+    assert lib.mcs_kmeans_workspace(0, 8) == 0
+    km = lambda n=1000, D=128, k=8, rounds=20, ws=W, nb=kws: lib.mcs_kmeans(A, B_, n, D, k, rounds, C_, D_, E_,
+                                                                          0x60000, ws, nb, None)
+    assert km(D=96) == c["MCS_E_HEAD_DIM"]
+    assert km(k=0) == c["MCS_E_ARG"] and km(k=1001) == c["MCS_E_ARG"]
+    assert km(rounds=0) == c["MCS_E_ARG"]
+    assert km(n=0) == c["MCS_E_SHAPE"] and km(n=1 << 24) == c["MCS_E_SHAPE"]   # n * D >= 2^31
+    assert km(nb=kws - 1) == c["MCS_E_WORKSPACE"]
+    assert km(ws=W + 4) == c["MCS_E_ALIGN"]
 
 
 def test_group_workspace_grows_with_partials(lib):
