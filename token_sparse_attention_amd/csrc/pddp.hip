@@ -62,8 +62,8 @@ struct MomentLds {
 
 template <int D>
 __device__ void node_moments(const uint16_t* __restrict__ qh, const int32_t* __restrict__ ph,
-                             int N, int m0, int m1, MomentLds<D>& L, f32x16_t* acc,
-                             float* sumx) {
+                             int N, int m0, int m1, MomentLds<D>& L, int32_t* __restrict__ ids,
+                             f32x16_t* acc, float* sumx) {
   constexpr int CH = D / 8;
   constexpr int NBLK = (D / 32) * (D / 32) / 4;
   constexpr int PAIRS = (MSTEP / 4) * CH;    // (quad of 4 queries, chunk)
@@ -76,13 +76,17 @@ __device__ void node_moments(const uint16_t* __restrict__ qh, const int32_t* __r
 #pragma unroll
   for (int e = 0; e < 8; ++e) sumx[e] = 0.f;
 
+  // The ids of [m0, m1) (at most CHUNK_M) go to LDS first, so that every row
+  // load below is a single global load (not an id load followed by a row
+  // load); the rows of step st + 1 are loaded while step st is computed.
+  for (int i = tid; i < m1 - m0; i += PD_NT) ids[i] = clamp_id(ph[m0 + i], N);
+  __syncthreads();
   u32x4_t xr[4];
   auto load = [&](int base) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = base + quad * 4 + r;
-      xr[r] = (loader && m < m1) ? ldg16(qh + (size_t)clamp_id(ph[m], N) * D + chunk * 8)
-                                 : zero_u32x4();
+      xr[r] = (loader && m < m1) ? ldg16(qh + (size_t)ids[m - m0] * D + chunk * 8) : zero_u32x4();
     }
   };
   auto store = [&](int buf) {
@@ -150,7 +154,9 @@ template <int D>
 __global__ __launch_bounds__(PD_NT) void pddp_moments(PddpParams p) {
   constexpr int NBLK = (D / 32) * (D / 32) / 4;
   __shared__ MomentLds<D> L;
+  // the per-thread sums of x, and before them the chunk's ids
   __shared__ float sred[PD_NT / (D / 8)][D];
+  static_assert(PD_NT / (D / 8) * D >= CHUNK_M, "ids of a chunk fit");
   const int c = blockIdx.x, slot = blockIdx.y, bh = blockIdx.z;
   int off, n, g;
   if (!node_by_rank(p.N, p.C, p.level, slot, off, n, g)) return;
@@ -160,7 +166,8 @@ __global__ __launch_bounds__(PD_NT) void pddp_moments(PddpParams p) {
   const size_t head = (size_t)bh * p.N;
   f32x16_t acc[NBLK];
   float sumx[8];
-  node_moments<D>(p.q + head * D, p.perm + head + off, p.N, m0, m1, L, acc, sumx);
+  node_moments<D>(p.q + head * D, p.perm + head + off, p.N, m0, m1, L, reinterpret_cast<int32_t*>(&sred[0][0]),
+                  acc, sumx);
 
   float* __restrict__ out = p.part + ((size_t)bh * p.slots + (size_t)slot * p.cpn + c) * (D * D + D);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lq = lane & 31, hh = lane >> 5;
@@ -209,15 +216,17 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   constexpr int RB = D / 32;
   constexpr int CH = D / 8;
   __shared__ MomentLds<D> L;
-  __shared__ float sred[MSTEP / 4][D];
+  // the per-thread sums of x, and before them the ids of the node's queries
+  // (nodes here hold at most CHUNK_M queries)
+  __shared__ float sred[(MSTEP / 4) * D >= CHUNK_M ? MSTEP / 4 : CHUNK_M / D][D];
   __shared__ float part[2][RB][D];
   __shared__ float mu[D];
-  // per wave: alpha, beta of the Lanczos recurrence and the tridiagonal
-  // solve's pivots and vector (every wave holds the same recurrence and runs
-  // the same solve, so all take the same stop decision without a barrier)
+  // per wave: alpha, beta of the Lanczos recurrence (every wave holds the same
+  // recurrence and runs the same convergence test, so all take the same stop
+  // decision without a barrier); the final solve's pivots and vector (wave 0)
   constexpr int NWAVE = PD_NT / 64;
   __shared__ float tri[NWAVE][2][KRYLOV_MAX];
-  __shared__ double tri_d[NWAVE][KRYLOV_MAX], tri_x[NWAVE][KRYLOV_MAX];
+  __shared__ double tri_d[KRYLOV_MAX], tri_x[KRYLOV_MAX];
   __shared__ int ish[2];
   constexpr int NV = D / 64;                     // vector components per lane
   static_assert(sizeof(MomentLds<D>) >= sizeof(float) * KRYLOV_MAX * D, "basis must fit the staging LDS");
@@ -250,7 +259,8 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     if (tid < D) mu[tid] = msum;
   } else {
     float sumx[8];
-    node_moments<D>(p.q + head * D, p.perm + head + off, p.N, 0, n, L, acc, sumx);
+    node_moments<D>(p.q + head * D, p.perm + head + off, p.N, 0, n, L, reinterpret_cast<int32_t*>(&sred[0][0]),
+                    acc, sumx);
     if (tid < (MSTEP / 4) * CH) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) sred[tid / CH][(tid % CH) * 8 + e] = sumx[e];
@@ -423,30 +433,34 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     for (int k = 0; k < NV; ++k) wv[k] -= dw[k];
     after = before - hsq;
   };
-  // The top eigenpair (theta, s) of the mm x mm tridiagonal T =
-  // tridiag(beta, alpha, beta) held in this wave's arrays: s goes to tx,
-  // theta (from above, to the multisection's resolution) is returned.  The
-  // recurrences are sequential in i and run on wave-uniform values: alpha_i
-  // and beta_i sit in lane i and are broadcast with readlane, reciprocals are
-  // v_rcp_f64 refined by one Newton step (relative error ~1e-14), and the
-  // pivots of the inverse iteration are formed once for both of its sweeps.
+  // The small tridiagonal eigenproblem T = tridiag(beta, alpha, beta): the
+  // recurrences are sequential in i and run on wave-uniform values, with
+  // reciprocals from v_rcp_f64 refined by one Newton step (relative error
+  // ~1e-14).
   float* const ta = tri[w][0];
   float* const tb = tri[w][1];
-  double* const td = tri_d[w];
-  double* const tx = tri_x[w];
+  double* const td = tri_d;
+  double* const tx = tri_x;
   auto rcp64 = [](double d) {
     const double r = __builtin_amdgcn_rcp(d);
     return fma(r, fma(-d, r, 1.0), r);
   };
-  auto top_pair = [&](int mm) -> double {
-    const float al = lane < mm ? ta[lane] : 0.f;
-    const float bl = lane < mm ? tb[lane] : 0.f;
-    auto a_at = [&](int i) { return (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), i)); };
-    auto b_at = [&](int i) { return (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl), i)); };
-    // Gershgorin interval, then multisection on Sturm counts: lane l counts
-    // the eigenvalues below lo + (hi - lo) (l + 1) / 65, and the interval
-    // shrinks to the two shifts around the largest eigenvalue.
-    double lo = INFINITY, hi = -INFINITY;
+  // alpha_i and beta_i of this wave's arrays, one per lane, broadcast with readlane
+  float al = 0.f, bl = 0.f;
+  auto load_tri = [&](int mm) {
+    al = lane < mm ? ta[lane] : 0.f;
+    bl = lane < mm ? tb[lane] : 0.f;
+  };
+  auto a_at = [&](int i) { return (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), i)); };
+  auto b_at = [&](int i) { return (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl), i)); };
+  // Gershgorin interval, then multisection on Sturm counts: lane l counts the
+  // eigenvalues below lo + (hi - lo) (l + 1) / 65, and the interval shrinks to
+  // the two shifts around the largest eigenvalue, 5 times.  hi bounds it from
+  // above.
+  auto bracket = [&](int mm, double& lo, double& hi) {
+    load_tri(mm);
+    lo = INFINITY;
+    hi = -INFINITY;
     for (int i = 0; i < mm; ++i) {
       const double r = (i > 0 ? fabs(b_at(i - 1)) : 0.0) + (i + 1 < mm ? fabs(b_at(i)) : 0.0);
       lo = fmin(lo, a_at(i) - r);
@@ -475,6 +489,34 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
         }
       }
     }
+  };
+  // |s_last| of the unit eigenvector of T for the eigenvalue th: rows mm-1
+  // down to 1 of (T - th) s = 0 solved from the end with s_{mm-1} = 1.  For a
+  // converged top pair the components grow towards the start, the stable
+  // direction of this recurrence, and |s_last| = 1 / |s|.
+  auto last_component = [&](int mm, double th) {
+    double sp = 0.0, sc = 1.0, n2 = 1.0, last = 1.0;
+    for (int i = mm - 1; i >= 1; --i) {
+      const double bi = i + 1 < mm ? b_at(i) : 0.0;
+      const double sn = -((a_at(i) - th) * sc + bi * sp) * rcp64(b_at(i - 1));
+      sp = sc;
+      sc = sn;
+      n2 = fma(sn, sn, n2);
+      if (n2 > 1e200) {                 // rescale the whole vector
+        sp *= 1e-100;
+        sc *= 1e-100;
+        last *= 1e-100;
+        n2 *= 1e-200;
+      }
+    }
+    return last / sqrt(n2);
+  };
+  // The top eigenpair (theta, s) of the mm x mm tridiagonal in this wave's
+  // arrays, for the final direction (wave 0): s goes to tx, theta (from above,
+  // to the multisection's resolution) is returned.
+  auto top_pair = [&](int mm) -> double {
+    double lo, hi;
+    bracket(mm, lo, hi);
     if (mm == 1) {
       if (lane == 0) tx[0] = 1.0;
       return a_at(0);
@@ -582,8 +624,9 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     // stop if the top Ritz pair of T (j + 1 steps) has converged: its
     // residual |C y - theta y| is beta_j |s_last|
     if (j + 1 == STOP_AT && j + 1 < steps) {
-      const double th = top_pair(j + 1);
-      if ((double)bnew * fabs(tx[j]) <= STOP_TOL * fabs(th)) break;
+      double lo, hi;
+      bracket(j + 1, lo, hi);
+      if ((double)bnew * last_component(j + 1, hi) <= STOP_TOL * fabs(hi)) break;
     }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
