@@ -712,21 +712,33 @@ __global__ __launch_bounds__(PD_NT) void pddp_project(PddpParams p) {
   const float muv = dv[D];
   const uint16_t* __restrict__ qh = p.q + head * D;
   const int32_t* __restrict__ ph = p.perm + head + off;
-  // UR rows per thread and pass, their loads issued together
-  constexpr int UR = 4;
-  for (int base = m0; base < m1; base += RPP * UR) {
-    int id[UR];
-    u32x4_t x[UR];
+  // UR rows per thread and pass, their loads issued together.  Pipelined:
+  // the rows of the next pass are in flight while this pass is computed, and
+  // the ids of the pass after that are loaded beside them.
+  constexpr int UR = 4, STEP = RPP * UR;
+  int id[UR], idn[UR] = {};
+  u32x4_t x[UR], xn[UR];
+#pragma unroll
+  for (int u = 0; u < UR; ++u) xn[u] = zero_u32x4();
+  auto load_ids = [&](int base, int (&ids)[UR]) {
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       const int m = base + u * RPP + sub;
-      id[u] = m < m1 ? ph[m] : 0;
+      ids[u] = m < m1 ? ph[m] : 0;
     }
+  };
+  auto load_rows = [&](int base, const int (&ids)[UR], u32x4_t (&xs)[UR]) {
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       const int m = base + u * RPP + sub;
-      x[u] = m < m1 ? ldg16(qh + (size_t)clamp_id(id[u], p.N) * D + chunk * 8) : zero_u32x4();
+      xs[u] = m < m1 ? ldg16(qh + (size_t)clamp_id(ids[u], p.N) * D + chunk * 8) : zero_u32x4();
     }
+  };
+  load_ids(m0, id);
+  load_rows(m0, id, x);
+  if (m0 + STEP < m1) load_ids(m0 + STEP, idn);
+  for (int base = m0; base < m1; base += STEP) {
+    if (base + STEP < m1) load_rows(base + STEP, idn, xn);
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       const int m = base + u * RPP + sub;
@@ -743,6 +755,12 @@ __global__ __launch_bounds__(PD_NT) void pddp_project(PddpParams p) {
         p.tmp[head + off + m] = id[u];
       }
     }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      id[u] = idn[u];
+      x[u] = xn[u];
+    }
+    if (base + 2 * STEP < m1) load_ids(base + 2 * STEP, idn);
   }
 }
 
