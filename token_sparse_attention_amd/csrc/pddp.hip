@@ -45,10 +45,12 @@ constexpr int DEFAULT_STEPS = 32;  // Lanczos steps (Krylov dimension) by defaul
 constexpr int KRYLOV_MAX = 64;     // most Lanczos steps; the basis fills the moment staging LDS
 // One convergence test of the Lanczos direction, after STOP_AT steps: the
 // iteration ends there when the Ritz residual is below STOP_TOL times the
-// Ritz value (a test costs about three steps, so one well-placed test saves
-// more than frequent ones).
+// Ritz value.  The test's eigenvalue bracket takes TEST_ROUNDS multisection
+// rounds (about 1e-5 relative, plenty for the residual estimate); the final
+// solve takes five.
 constexpr int STOP_AT = 16;
 constexpr double STOP_TOL = 1e-6;
+constexpr int TEST_ROUNDS = 3;
 
 __device__ __forceinline__ int swz_st(int d) { return (d >> 1) & 7; }
 
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   // eigenvalues below lo + (hi - lo) (l + 1) / 65, and the interval shrinks to
   // the two shifts around the largest eigenvalue, 5 times.  hi bounds it from
   // above.
-  auto bracket = [&](int mm, double& lo, double& hi) {
+  auto bracket = [&](int mm, int rounds, double& lo, double& hi) {
     load_tri(mm);
     lo = INFINITY;
     hi = -INFINITY;
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
       hi = fmax(hi, a_at(i) + r);
     }
     if (mm > 1 && hi > lo) {
-      for (int round = 0; round < 5; ++round) {
+      for (int round = 0; round < rounds; ++round) {
         const double x = lo + (hi - lo) * (double)(lane + 1) / 65.0;
         int cnt = 0;
         double d = 1.0;
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
   // to the multisection's resolution) is returned.
   auto top_pair = [&](int mm) -> double {
     double lo, hi;
-    bracket(mm, lo, hi);
+    bracket(mm, 5, lo, hi);
     if (mm == 1) {
       if (lane == 0) tx[0] = 1.0;
       return a_at(0);
@@ -625,7 +627,7 @@ __global__ __launch_bounds__(PD_NT) void pddp_direction(PddpParams p) {
     // residual |C y - theta y| is beta_j |s_last|
     if (j + 1 == STOP_AT && j + 1 < steps) {
       double lo, hi;
-      bracket(j + 1, lo, hi);
+      bracket(j + 1, TEST_ROUNDS, lo, hi);
       if ((double)bnew * last_component(j + 1, hi) <= STOP_TOL * fabs(hi)) break;
     }
 #pragma unroll
