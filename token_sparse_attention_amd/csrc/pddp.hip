@@ -21,7 +21,7 @@
 // tie in projection is broken by query id simply by position.
 //
 // Per level, for all nodes of all heads at once:
-//   pddp_moments   (large nodes only) chunks of 2048 queries -> partial
+//   pddp_moments   (large nodes only) equal chunks of <= 2048 queries -> partial
 //                  sum(x) and sum(x x^T) on bf16 MFMA with fp32 accumulation;
 //   pddp_direction one workgroup per node: moments (summed partials, or
 //                  computed directly for small nodes) -> covariance ->
@@ -162,9 +162,12 @@ __global__ __launch_bounds__(PD_NT) void pddp_moments(PddpParams p) {
   const int c = blockIdx.x, slot = blockIdx.y, bh = blockIdx.z;
   int off, n, g;
   if (!node_by_rank(p.N, p.C, p.level, slot, off, n, g)) return;
-  const int m0 = c * CHUNK_M;
-  if (m0 >= n) return;
-  const int m1 = min(n, m0 + CHUNK_M);
+  // the node's ceil(n / CHUNK_M) chunks, of equal size up to one query
+  const int nch = (n + CHUNK_M - 1) / CHUNK_M;
+  const int span = (n + nch - 1) / nch;
+  const int m0 = c * span;
+  if (c >= nch || m0 >= n) return;
+  const int m1 = min(n, m0 + span);
   const size_t head = (size_t)bh * p.N;
   f32x16_t acc[NBLK];
   float sumx[8];
