@@ -42,7 +42,8 @@ def test_dense_matches_oracle(mcs, B, H, N, D):
     ref_o, ref_lse = oracle.dense_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), scale)
     assert_output_close(bf16_to_f64(o), ref_o, "dense O")
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=2e-3)
-    assert torch.equal(o, o_nolse)
+    # without the LSE the kernel defers its row max (another rounding order)
+    assert_output_close(bf16_to_f64(o_nolse), ref_o, "dense O without LSE")
 
 
 def test_dense_large_logits(mcs):
@@ -83,6 +84,30 @@ def test_sparse_reference_moves_many_times(mcs, ascending):
     o = mcs.sparse_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), to_dev(perm), to_dev(idx), C, scale=1.0,
                         out_dtype=torch.float32)
     ref = oracle.sparse_attention_bh(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), perm, idx, C, 1.0)
+    assert_output_close(o.cpu().numpy().astype(np.float64), ref, "sparse O (fp32 out)")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_reference_jumps_past_fp32_range(mcs, D):
+    """Each 64-key tile outscores the one before by about 170 in log2 units,
+    so exponentials taken against the old reference overflow to inf: the
+    kernels without an LSE output must see that in the tile's P sum, move the
+    reference and take the tile's exponentials again (dense and sparse)."""
+    N, C, K = 400, 128, 300
+    q, k, v = synth.growing_scores(N, D, seed=35, step=40.0)
+    qf, kf, vf = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
+    ref_o, ref_lse = oracle.dense_attention_bh(qf, kf, vf, 1.0)
+    assert ref_lse.min() > 300.0   # every row ends > 2^128 (in P) above its first tile's scores
+    o32 = mcs.dense_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), 1.0, out_dtype=torch.float32)
+    assert_output_close(o32.cpu().numpy().astype(np.float64), ref_o, "dense O (fp32 out)")
+    o, lse = mcs.dense_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), 1.0, want_lse=True)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=2e-3)
+    G = accounting.num_groups(N, C)
+    perm = synth.random_perm(1, 1, N, seed=36)
+    idx = synth.random_index_sets(1, 1, G, K, N, seed=37)
+    o = mcs.sparse_attn(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), to_dev(perm), to_dev(idx), C, scale=1.0,
+                        out_dtype=torch.float32)
+    ref = oracle.sparse_attention_bh(qf, kf, vf, perm, idx, C, 1.0)
     assert_output_close(o.cpu().numpy().astype(np.float64), ref, "sparse O (fp32 out)")
 
 

@@ -26,8 +26,11 @@
 //     with lane L^32 for the running maximum.  Base-2 softmax with
 //     scale*log2(e) folded into one FMA per score.  The running maximum is
 //     only moved (and O rescaled) when a new score exceeds it by more than
-//     2^8, so most tiles skip the rescale; P stays <= 256, exact in bf16
-//     range, and the final division by the row sum cancels the offset.
+//     2^8, so most tiles skip the rescale; P stays small (<= 2^13), well in
+//     bf16 range, and the final division by the row sum cancels the offset.
+//     Kernels without an LSE output defer even the row max: they take the
+//     exponentials against the current maximum and let the tile's P sum
+//     show the rare tile that must move it (that tile is then redone).
 //   * O^T += V^T P^T on MFMA, P^T taken straight from the S^T accumulators and
 //     V^T fragments read with the LDS transpose load ds_read_b64_tr_b16.  O
 //     is normalised by the sum of the same bf16-rounded P that enter the
@@ -54,6 +57,7 @@ constexpr int KT = 64;          // keys per KV tile
 #define MCS_SCHED_VALU 4             // VALU instructions interleaved after each S MFMA
 #endif
 constexpr float kRescaleSlack = 8.f;   // log2 of the largest unscaled P
+constexpr float kDeferredLimit = 8192.f;  // a lane's 32 values of one tile, each <= 2^8
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t* lds_bf16x4_ptr;
@@ -235,29 +239,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   };
 
   // ---- online softmax of one tile's scores (base 2), one query per lane ----
-  // part 1: row max, and the (rare, wave-uniform) move of the reference max
-  auto softmax_max = [&](f32x16_t (&sacc)[2]) {
+  // The reference maximum m_run moves, and O and the row sums are rescaled,
+  // only when a score exceeds it by more than 2^8 (wave-uniform, rare).
+  auto tile_max = [&](const f32x16_t (&sacc)[2]) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = halves_max(mx) * p.sl2;
-    // move the reference maximum only when a score exceeds it by > 2^slack
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      if (LSE) l_lse *= alpha;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[b][e] *= alpha;
-    }
+    return halves_max(mx) * p.sl2;
   };
-  // part 2: P = exp2(s*scale*log2e - m) as bf16 MFMA fragments, row sums
-  auto softmax_p = [&](f32x16_t (&sacc)[2], bf16x8_t (&pf)[KT / 16]) {
+  auto move_max = [&](float mx) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+    if (LSE) l_lse *= alpha;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[b][e] *= alpha;
+  };
+  // eager form (kernels with an LSE output, and the last tile): the row max
+  // first, then the exponentials
+  auto softmax_max = [&](f32x16_t (&sacc)[2]) {
+    const float mx = tile_max(sacc);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) move_max(mx);
+  };
+  // P = exp2(s*scale*log2e - m) as bf16 MFMA fragments; lsum accumulates the
+  // sum of the bf16-rounded P, l_lse (LSE kernels) the exact one
+  auto softmax_p = [&](f32x16_t (&sacc)[2], bf16x8_t (&pf)[KT / 16], float& lsum) {
     const float mneg = -m_run;
 #pragma unroll
     for (int s = 0; s < KT / 16; ++s) {
@@ -268,11 +279,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
         const float x0 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd], p.sl2, mneg));
         const float x1 = fast_exp2(fmaf(sacc[kb][e0 + 2 * wd + 1], p.sl2, mneg));
         pw[wd] = pack_bf16x2(x0, x1);
-        l_run = add_bf16_pair(pw[wd], l_run);
+        lsum = add_bf16_pair(pw[wd], lsum);
         if (LSE) l_lse += x0 + x1;
       }
       pf[s] = as_bf16x8(pw);
     }
+  };
+  // deferred form (kernels without an LSE output): the exponentials are taken
+  // against the current reference first, so no row max precedes them; the
+  // tile's P sum then shows whether a score exceeded the reference by more
+  // than 2^8 (sum above 32 * 2^8, an overflow, or the first tile, whose
+  // reference is -inf), and only such a tile moves the maximum and takes its
+  // exponentials again.  P stays <= 2^13.
+  auto softmax_check = [&](f32x16_t (&sacc)[2], bf16x8_t (&pf)[KT / 16], float lt) {
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kDeferredLimit)) != 0) {
+      move_max(tile_max(sacc));
+      lt = 0.f;
+      softmax_p(sacc, pf, lt);
+    }
+    l_run += lt;
   };
   // O^T += V^T P^T with the V tile in BUF; V^T fragments by LDS transpose
   // reads (lane group lane/16 reads 4 consecutive key rows, lane i%16 gets
@@ -296,10 +321,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
 
   // Software pipeline.  Iteration t (buffer parity P = t & 1) waits for K_{t+1}
   // and V_t, issues the gathers of V_{t+1} (into V buffer P^1) and K_{t+2}
-  // (into K buffer P), takes the row max of S_t, then in one branch-free
-  // block computes S_{t+1} = K_{t+1} Q^T on MFMA interleaved with the
-  // exponentials of S_t on the VALU, and O += V_t P_t.  Only the last tile
-  // can be partial; it is peeled off and masked.
+  // (into K buffer P), takes the row max of S_t (eager form only), then in
+  // one branch-free block computes S_{t+1} = K_{t+1} Q^T on MFMA interleaved
+  // with the exponentials of S_t on the VALU, and O += V_t P_t.  Only the
+  // last tile can be partial; it is peeled off and masked.
   uint32_t rowk[IPW], rowv[IPW];
   auto step_head = [&](auto par_c, int t) {
     constexpr int P = decltype(par_c)::value;
@@ -316,23 +341,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   };
   auto steady_step = [&](auto par_c, int t, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
     constexpr int P = decltype(par_c)::value;
-    step_head(par_c, t);
-    softmax_max(s_cur);
-    bf16x8_t pf[KT / 16];
-    softmax_p(s_cur, pf);
-    compute_s(ic<P ^ 1>{}, s_nxt);
-    pv(ic<P>{}, pf);
-    // interleave: K fragment reads run LOOKAHEAD MFMAs ahead; each S MFMA is
-    // followed by a share of the exponentials' VALU work; then the PV MFMAs
-    // with their transpose reads, also run ahead
     constexpr int LOOKAHEAD = MCS_SCHED_LOOKAHEAD;
-    __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);        // DS read
+    // K fragment reads run LOOKAHEAD MFMAs ahead; each S MFMA is followed by
+    // a share of the exponentials' VALU work
+    auto interleave_s = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);        // DS read
 #pragma unroll
-    for (int i = 0; i < 2 * KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, MCS_SCHED_VALU, 0); // VALU
-      if (i + LOOKAHEAD < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, MCS_SCHED_VALU, 0); // VALU
+        if (i + LOOKAHEAD < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    step_head(par_c, t);
+    bf16x8_t pf[KT / 16];
+    if constexpr (LSE) {
+      softmax_max(s_cur);
+      softmax_p(s_cur, pf, l_run);
+      compute_s(ic<P ^ 1>{}, s_nxt);
+      pv(ic<P>{}, pf);
+      interleave_s();
+    } else {
+      float lt = 0.f;
+      softmax_p(s_cur, pf, lt);
+      compute_s(ic<P ^ 1>{}, s_nxt);
+      interleave_s();
+      softmax_check(s_cur, pf, lt);
+      pv(ic<P>{}, pf);
     }
+    // then the PV MFMAs with their transpose reads, also run ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * LOOKAHEAD, 0);    // DS read (transpose)
 #pragma unroll
     for (int i = 0; i < (KT / 16) * DB; ++i) {
@@ -355,7 +392,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
     }
     softmax_max(s_cur);
     bf16x8_t pf[KT / 16];
-    softmax_p(s_cur, pf);
+    softmax_p(s_cur, pf, l_run);
     pv(ic<P>{}, pf);
   };
 
