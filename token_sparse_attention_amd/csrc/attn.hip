@@ -149,15 +149,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int r = (w * IPW + j) * ROWS_PER_INSTR + lrow;
-      const int kp = tile * KT + r;
-      int row;
-      if (SPARSE) row = ring[(tile % (2 * IDS_CHUNK)) * KT + r];
-      else row = kp < nkeys ? kp : -1;   // -1: past the end -> zero rows
+      const int row = ring[(tile % (2 * IDS_CHUNK)) * KT + r];
       // an id outside [0, N) gets an offset past the descriptor's end (N*D*2 <
       // 2^31), so it reads a zero row; the product would wrap for large ids
       rowoff[j] = (uint32_t)row < (uint32_t)p.N ? (uint32_t)row * (uint32_t)ROWB + coff[j] : 0x80000000u;
     }
   };
+  // Dense: a tile's rows are consecutive, so each load's offset is a per-lane
+  // constant (its row in the tile and chunk) plus the tile's base, a scalar;
+  // rows past N fall past the descriptor's end and read zeros.
+  uint32_t doff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) doff[j] = (uint32_t)(((w * IPW + j) * ROWS_PER_INSTR + lrow) * ROWB) + coff[j];
   // refill ring half (chunk & 1) with the ids of tiles [chunk*IDS_CHUNK, +IDS_CHUNK)
   __amdgpu_buffer_rsrc_t rids;
   if (SPARSE) rids = head_rsrc(ids, (uint32_t)p.K * 4u);
@@ -171,18 +174,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
       dma16(rids, (uint32_t)(chunk * BYTES + blk * 1024 + lane * 16), half + blk * 1024);
     }
   };
-  // K tiles live in lds[*][0], V tiles in lds[*][1]; K runs one tile ahead of V
-  auto issue_k = [&](auto buf_c, const uint32_t (&rowoff)[IPW]) {
-    constexpr int BUF = decltype(buf_c)::value;
+  // K tiles live in lds[*][0], V tiles in lds[*][1]; K runs one tile ahead of
+  // V.  `tile` is the key tile the rows belong to (dense), rowoff the gathered
+  // rows' offsets (sparse).
+  auto issue_rows = [&](__amdgpu_buffer_rsrc_t r, const uint32_t (&rowoff)[IPW], int tile, char* dst) {
+    if constexpr (SPARSE) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j)
-      dma16(rk, rowoff[j], lbase + BUF * STAGE_BYTES + (w * IPW + j) * 1024);
+      for (int j = 0; j < IPW; ++j) dma16(r, rowoff[j], dst + (w * IPW + j) * 1024);
+    } else {
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)tile * (uint32_t)TILE_BYTES);
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) dma16s(r, doff[j], soff, dst + (w * IPW + j) * 1024);
+    }
   };
-  auto issue_v = [&](auto buf_c, const uint32_t (&rowoff)[IPW]) {
+  auto issue_k = [&](auto buf_c, const uint32_t (&rowoff)[IPW], int tile) {
     constexpr int BUF = decltype(buf_c)::value;
-#pragma unroll
-    for (int j = 0; j < IPW; ++j)
-      dma16(rv, rowoff[j], lbase + BUF * STAGE_BYTES + TILE_BYTES + (w * IPW + j) * 1024);
+    issue_rows(rk, rowoff, tile, lbase + BUF * STAGE_BYTES);
+  };
+  auto issue_v = [&](auto buf_c, const uint32_t (&rowoff)[IPW], int tile) {
+    constexpr int BUF = decltype(buf_c)::value;
+    issue_rows(rv, rowoff, tile, lbase + BUF * STAGE_BYTES + TILE_BYTES);
   };
 
   // ---- per-lane LDS read offsets (buffer, key block and k-step are immediates) ----
@@ -325,18 +336,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   // one branch-free block computes S_{t+1} = K_{t+1} Q^T on MFMA interleaved
   // with the exponentials of S_t on the VALU, and O += V_t P_t.  Only the
   // last tile can be partial; it is peeled off and masked.
-  uint32_t rowk[IPW], rowv[IPW];
+  uint32_t rowk[IPW] = {}, rowv[IPW] = {};    // sparse only
   auto step_head = [&](auto par_c, int t) {
     constexpr int P = decltype(par_c)::value;
     wait_vmem_all();
     __syncthreads();
     if (SPARSE && t % IDS_CHUNK == 0 && t + IDS_CHUNK < ntiles) refill_ids(t / IDS_CHUNK + 1);
-    if (t + 1 < ntiles) issue_v(ic<P ^ 1>{}, rowv);
+    if (t + 1 < ntiles) issue_v(ic<P ^ 1>{}, rowv, t + 1);
     if (t + 2 < ntiles) {
-      fetch_ids(t + 2, rowk);
-      issue_k(ic<P>{}, rowk);
+      if (SPARSE) fetch_ids(t + 2, rowk);
+      issue_k(ic<P>{}, rowk, t + 2);
+      if (SPARSE)
 #pragma unroll
-      for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
+        for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
     }
   };
   auto steady_step = [&](auto par_c, int t, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
@@ -401,14 +413,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
     wait_vmem_all();
     __syncthreads();
   }
-  fetch_ids(0, rowk);
-  issue_k(ic<0>{}, rowk);
-  issue_v(ic<0>{}, rowk);
+  if (SPARSE) fetch_ids(0, rowk);
+  issue_k(ic<0>{}, rowk, 0);
+  issue_v(ic<0>{}, rowk, 0);
   if (ntiles > 1) {
-    fetch_ids(1, rowk);
-    issue_k(ic<1>{}, rowk);
+    if (SPARSE) fetch_ids(1, rowk);
+    issue_k(ic<1>{}, rowk, 1);
+    if (SPARSE)
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
+      for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
   }
   wait_vmem_all();
   __syncthreads();

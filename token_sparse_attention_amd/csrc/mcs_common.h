@@ -215,6 +215,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, v
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
 }
 
+// dma16 with a wave-uniform byte offset soff added to voff (the buffer's
+// range check covers the sum: a load at or past the descriptor's end reads
+// zeros; the LDS placement does not depend on soff).
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_t)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
+}
+
 // One 4-byte buffer load per lane written straight to LDS: the wave writes
 // 256 bytes at lds (wave-uniform) + 4 * lane (same ordering rules as dma16).
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {

@@ -118,10 +118,9 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
     coff[j] = (uint32_t)(r * ROWB + (((lane % CH) ^ swz<D>(r)) << 4));
   }
   auto issue = [&](int tile, int buf) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)tile * (uint32_t)TILE_BYTES);
 #pragma unroll
-    for (int j = 0; j < IPW; ++j)
-      dma16(rk, (uint32_t)tile * (uint32_t)TILE_BYTES + coff[j],
-            lbase + buf * TILE_BYTES + (w * IPW + j) * 1024);
+    for (int j = 0; j < IPW; ++j) dma16s(rk, coff[j], soff, lbase + buf * TILE_BYTES + (w * IPW + j) * 1024);
   };
   // B fragment of k-step ks for key column lq of a 32-key block
   uint32_t koff[KSTEPS];
