@@ -149,10 +149,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int r = (w * IPW + j) * ROWS_PER_INSTR + lrow;
-      const int row = ring[(tile % (2 * IDS_CHUNK)) * KT + r];
-      // an id outside [0, N) gets an offset past the descriptor's end (N*D*2 <
-      // 2^31), so it reads a zero row; the product would wrap for large ids
-      rowoff[j] = (uint32_t)row < (uint32_t)p.N ? (uint32_t)row * (uint32_t)ROWB + coff[j] : 0x80000000u;
+      const uint32_t row = (uint32_t)ring[(tile % (2 * IDS_CHUNK)) * KT + r];
+      // an id outside [0, N) (negative ones included, as unsigned) is clamped
+      // to N, whose offset lies past the descriptor's end (N*D*2 < 2^31), so
+      // it reads a zero row; the product of a larger id could wrap
+      rowoff[j] = __builtin_elementwise_min(row, (uint32_t)p.N) * (uint32_t)ROWB + coff[j];
     }
   };
   // Dense: a tile's rows are consecutive, so each load's offset is a per-lane
@@ -336,19 +337,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
   // one branch-free block computes S_{t+1} = K_{t+1} Q^T on MFMA interleaved
   // with the exponentials of S_t on the VALU, and O += V_t P_t.  Only the
   // last tile can be partial; it is peeled off and masked.
-  uint32_t rowk[IPW] = {}, rowv[IPW] = {};    // sparse only
+  // Sparse: the gathered rows' offsets of tile t stay in offs[t & 1] from
+  // its K gather (two steps ahead) to its V gather (one step ahead).
+  uint32_t offs[2][IPW] = {};
   auto step_head = [&](auto par_c, int t) {
     constexpr int P = decltype(par_c)::value;
     wait_vmem_all();
     __syncthreads();
     if (SPARSE && t % IDS_CHUNK == 0 && t + IDS_CHUNK < ntiles) refill_ids(t / IDS_CHUNK + 1);
-    if (t + 1 < ntiles) issue_v(ic<P ^ 1>{}, rowv, t + 1);
+    if (t + 1 < ntiles) issue_v(ic<P ^ 1>{}, offs[P ^ 1], t + 1);
     if (t + 2 < ntiles) {
-      if (SPARSE) fetch_ids(t + 2, rowk);
-      issue_k(ic<P>{}, rowk, t + 2);
-      if (SPARSE)
-#pragma unroll
-        for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
+      if (SPARSE) fetch_ids(t + 2, offs[P]);
+      issue_k(ic<P>{}, offs[P], t + 2);
     }
   };
   auto steady_step = [&](auto par_c, int t, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2]) {
@@ -413,15 +413,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnParams p) {
     wait_vmem_all();
     __syncthreads();
   }
-  if (SPARSE) fetch_ids(0, rowk);
-  issue_k(ic<0>{}, rowk, 0);
-  issue_v(ic<0>{}, rowk, 0);
+  if (SPARSE) fetch_ids(0, offs[0]);
+  issue_k(ic<0>{}, offs[0], 0);
+  issue_v(ic<0>{}, offs[0], 0);
   if (ntiles > 1) {
-    if (SPARSE) fetch_ids(1, rowk);
-    issue_k(ic<1>{}, rowk, 1);
-    if (SPARSE)
-#pragma unroll
-      for (int j = 0; j < IPW; ++j) rowv[j] = rowk[j];
+    if (SPARSE) fetch_ids(1, offs[1]);
+    issue_k(ic<1>{}, offs[1], 1);
   }
   wait_vmem_all();
   __syncthreads();
