@@ -9,7 +9,8 @@
 //
 // group_mass_kernel: one workgroup per (head, group).  The group's C queries
 // (gathered by perm) stay in registers as MFMA A fragments; all N keys stream
-// through LDS in tiles of 64 (double buffered).  S = Q K^T on MFMA leaves one
+// through LDS in tiles of 64 (double buffered), starting at a tile taken from
+// the clock so that concurrent workgroups share their K tiles in L2.  S = Q K^T on MFMA leaves one
 // key per lane column, so each lane sums exp2(s*scale*log2e - lse_i*log2e)
 // over its 16 query rows; the two half-waves' sums and the C/32 waves combine
 // through LDS in a fixed order, one wave per tile in turn.  One fp32 mass row
@@ -37,6 +38,15 @@
 namespace mcs {
 
 constexpr int MKT = 64;  // keys per tile
+// Sweep alignment: workgroups start their key sweep at the chunk of
+// SWEEP_CHUNK tiles given by the 100 MHz clock, one chunk per SWEEP_TICKS
+// (about the time a workgroup takes for a chunk at full occupancy: 4 waves
+// per SIMD for C = 128, 2 for C = 64), so the workgroups resident on an XCD
+// read the same K tiles at about the same time.  The masses do not depend on
+// the order of the sweep.
+constexpr int SWEEP_CHUNK = 32;
+template <int NW>
+constexpr int sweep_ticks() { return NW == 4 ? 7000 : 3500; }
 
 struct MassParams {
   const uint16_t* q;
@@ -86,8 +96,7 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   const int hl = lb / p.G, g = lb - hl * p.G;
   const size_t head = (size_t)(p.bh0 + hl) * p.N;
   const uint16_t* __restrict__ qh = p.q + head * D;
-  const __amdgpu_buffer_rsrc_t rk = FUSED ? head_rsrc_uniform(p.k + head * D, (uint32_t)p.N * ROWB)
-                                          : head_rsrc(p.k + head * D, (uint32_t)p.N * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc_uniform(p.k + head * D, (uint32_t)p.N * ROWB);
 
   // A fragments: row lq of the wave's 32-query block
   const int qpos = g * p.C + w * 32 + lq;
@@ -148,10 +157,26 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
   // the mass of key `lane` of tile t: per wave, the two half-wave partial
   // sums added, then the waves summed in order.  Wave t % NW does it, so the
   // work rotates over the SIMDs.
-  auto store_tile = [&](int t) {
-    const int b = t & 1, blk = lane >> 5, lk = lane & 31;
-    const int key = t * MKT + lane;
-    if (w == (t & (NW - 1)) && key < p.N) {
+  const int ntiles = (p.N + MKT - 1) / MKT;
+  // sweep order: iteration i handles tile (i + t0) mod ntiles, t0 taken from
+  // the clock by one thread and shared
+  int t0;
+  {
+    __shared__ int t0_sh;
+    if (tid == 0) {
+      const int nchunks = (ntiles + SWEEP_CHUNK - 1) / SWEEP_CHUNK;
+      const uint64_t now = __builtin_amdgcn_s_memrealtime();
+      t0_sh = (int)((now / (uint64_t)sweep_ticks<NW>()) % (uint64_t)nchunks) * SWEEP_CHUNK;
+    }
+    __syncthreads();
+    t0 = __builtin_amdgcn_readfirstlane(t0_sh);
+    if (t0 >= ntiles) t0 = 0;
+  }
+  auto tile_of = [&](int i) { const int t = i + t0; return t >= ntiles ? t - ntiles : t; };
+  auto store_tile = [&](int i) {
+    const int b = i & 1, blk = lane >> 5, lk = lane & 31;
+    const int key = tile_of(i) * MKT + lane;
+    if (w == (i & (NW - 1)) && key < p.N) {
       float s = red[b][0][blk][lk] + red[b][0][blk][32 + lk];
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) s += red[b][ww][blk][lk] + red[b][ww][blk][32 + lk];
@@ -160,18 +185,17 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
     }
   };
 
-  // Step t: wait for K_t, barrier (K_{t-1} and the partial masses of tile
-  // t-1 are then free / complete), gather K_{t+1} into the other buffer,
-  // store tile t-1's mass, then S = Q K_t^T with the MFMA chains of the two
+  // Step t (tiles in sweep order): wait for K_t, barrier (K_{t-1} and the
+  // partial masses of tile t-1 are then free / complete), gather K_{t+1} into
+  // the other buffer, store tile t-1's mass, then S = Q K_t^T with the MFMA chains of the two
   // 32-key blocks alternating (independent accumulators back to back), then
   // the exponentials; the other waves on the SIMD fill the MFMA gaps.  The
   // loop is unrolled by the two buffers so all LDS offsets are immediates.
-  const int ntiles = (p.N + MKT - 1) / MKT;
   auto step = [&](auto buf_c, int t) {
     constexpr int BUF = decltype(buf_c)::value;
     wait_vmem_all();
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, BUF ^ 1);
+    if (t + 1 < ntiles) issue(tile_of(t + 1), BUF ^ 1);
     if (t > 0) store_tile(t - 1);
     const char* kt = lbase + BUF * TILE_BYTES;
     f32x16_t acc0 = zero16(), acc1 = zero16();
@@ -183,7 +207,7 @@ __global__ __launch_bounds__(NW * 64, 4) void group_mass_kernel(MassParams p) {
     red[BUF][w][0][lane] = block_mass(acc0);
     red[BUF][w][1][lane] = block_mass(acc1);
   };
-  issue(0, 0);
+  issue(tile_of(0), 0);
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
     step(std::integral_constant<int, 0>{}, t);
