@@ -146,7 +146,10 @@ def test_fused_select_equals_two_pass(mcs, N, D, C, K, dup):
     4-byte reads; the latter leaves no LDS for the gathered third-digit keys,
     so the counting read runs) and for D = 128, one past each (mcs_select takes
     the two-kernel route), K = N, and duplicated keys (equal masses in pairs,
-    so the tie rule decides at the K-th key)."""
+    so the tie rule decides at the K-th key).  Both kernels start each key
+    sweep at a tile taken from the clock (rows of more than 32 tiles), so the
+    calls sweep in different orders: equal ids also show that the masses do
+    not depend on where a sweep starts."""
     q = synth.gaussian((1, 1, N, D), 60 + N, 1.5)
     k = synth.gaussian((1, 1, N, D), 61 + N, 1.5)
     if dup:
