@@ -107,12 +107,11 @@ def test_sparse_reuse_sampled_groups(mcs, name, density):
             assert_output_close(o32[bh, members], ref, f"{name} s={density} head {bh} group {g}")
 
 
-@pytest.mark.parametrize("name", WORKLOADS)
-def test_select_sampled_groups(mcs, name):
+@pytest.mark.parametrize("name,density", list(_sparse_cases()))
+def test_select_sampled_groups(mcs, name, density):
     w = synth.WORKLOADS[name]
     d = _inputs(name)
-    s = w.densities[0]
-    K = accounting.k_from_density(s, w.N)
+    K = accounting.k_from_density(density, w.N)
     G = accounting.num_groups(w.N, w.C)
     scale = 1 / math.sqrt(w.D)
     # raster-order groups (perm = identity) are spatially coherent for the video workloads
@@ -130,7 +129,7 @@ def test_select_sampled_groups(mcs, name):
             _, lse_g = oracle.dense_attention(q[members], k, k, scale)   # only the LSE is used
             mass = oracle.probabilities(q[members], k, lse_g, scale).sum(axis=0)[None]
             ref = oracle.topk_indices(mass[0], K)[None]
-            assert_index_sets_match(got[bh, g:g + 1], ref, mass, K, f"{name} head {bh} group {g}")
+            assert_index_sets_match(got[bh, g:g + 1], ref, mass, K, f"{name} s={density} head {bh} group {g}")
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
