@@ -193,8 +193,8 @@ def test_tiny_anchor_and_reuse_in_full(mcs):
 CHAIN_REUSE_STEPS = {"tiny": 1, "small": 4, "large": 1, "long": 1, "asset3d": 9}
 
 
-@pytest.mark.parametrize("name", WORKLOADS)
-def test_chain_at_workload_size(mcs, name):
+@pytest.mark.parametrize("name,density", list(_sparse_cases()))
+def test_chain_at_workload_size(mcs, name, density):
     """The anchor step on the GPU's own upstream (GPU grouping -> dense + LSE ->
     selection on the GPU perm -> sparse -> residual), then the configuration's
     reuse steps on drifted inputs with the cached perm, ids and residual.  On
@@ -203,7 +203,7 @@ def test_chain_at_workload_size(mcs, name):
     benchmark)."""
     w = synth.WORKLOADS[name]
     d = _inputs(name)
-    K = accounting.k_from_density(w.densities[0], w.N)
+    K = accounting.k_from_density(density, w.N)
     G = accounting.num_groups(w.N, w.C)
     scale = 1 / math.sqrt(w.D)
     dq, dk, dv = d["dev"]["q"], d["dev"]["k"], d["dev"]["v"]
@@ -230,10 +230,10 @@ def test_chain_at_workload_size(mcs, name):
             _, lse_g = oracle.dense_attention(q[members], k, k, scale)
             mass = oracle.probabilities(q[members], k, lse_g, scale).sum(axis=0)[None]
             ref_ids = oracle.topk_indices(mass[0], K)[None]
-            assert_index_sets_match(idx[bh, g:g + 1], ref_ids, mass, K, f"{name} anchor head {bh} group {g}")
+            assert_index_sets_match(idx[bh, g:g + 1], ref_ids, mass, K, f"{name} s={density} anchor head {bh} group {g}")
             ref = oracle.sparse_attention(q[members], k, v, np.arange(members.size), idx[bh, g:g + 1], w.C, scale)
-            assert_output_close(o_sp32[bh, members], ref, f"{name} anchor sparse head {bh} group {g}")
-    print(f"[chain] {name}: anchor checked on heads {heads}, groups {groups}", flush=True)
+            assert_output_close(o_sp32[bh, members], ref, f"{name} s={density} anchor sparse head {bh} group {g}")
+    print(f"[chain] {name} s={density}: anchor checked on heads {heads}, groups {groups}", flush=True)
     x = d["x"]
     res_f64 = {bh: synth.to_f64(res[bh].view(torch.int16).cpu().numpy().view(np.uint16)) for bh in heads}
     for t in range(1, CHAIN_REUSE_STEPS[name] + 1):
@@ -248,6 +248,6 @@ def test_chain_at_workload_size(mcs, name):
                 members = permf[bh, g * w.C:(g + 1) * w.C]
                 ref = oracle.sparse_attention(q[members], k, v, np.arange(members.size), idx[bh, g:g + 1], w.C,
                                               scale, residual=res_f64[bh][members])
-                assert_output_close(ob[members], ref, f"{name} reuse step {t} head {bh} group {g}")
+                assert_output_close(ob[members], ref, f"{name} s={density} reuse step {t} head {bh} group {g}")
         del qt, kt, vt, o
-    print(f"[chain] {name}: {CHAIN_REUSE_STEPS[name]} reuse steps checked", flush=True)
+    print(f"[chain] {name} s={density}: {CHAIN_REUSE_STEPS[name]} reuse steps checked", flush=True)
