@@ -480,25 +480,33 @@ static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
 }
 
 template <int D, int NW, bool OUTF32>
-static hipError_t dispatch_attn(const AttnParams& p, bool sparse, bool res, bool lse, hipStream_t s) {
-  if (sparse) {
-    if (lse) return launch_attn<D, NW, true, false, true, OUTF32>(p, s);   // no residual (checked)
-    return res ? launch_attn<D, NW, true, true, false, OUTF32>(p, s)
-               : launch_attn<D, NW, true, false, false, OUTF32>(p, s);
-  }
-  return lse ? launch_attn<D, NW, false, false, true, OUTF32>(p, s)
-             : launch_attn<D, NW, false, false, false, OUTF32>(p, s);
+static hipError_t dispatch_sparse(const AttnParams& p, bool res, bool lse, hipStream_t s) {
+  if (lse) return launch_attn<D, NW, true, false, true, OUTF32>(p, s);   // no residual (checked)
+  return res ? launch_attn<D, NW, true, true, false, OUTF32>(p, s)
+             : launch_attn<D, NW, true, false, false, OUTF32>(p, s);
+}
+
+// The dense pass has no query groups: it always runs workgroups of 128 query
+// rows (four waves), so only those variants are built.
+template <int D, bool OUTF32>
+static hipError_t dispatch_dense(const AttnParams& p, bool lse, hipStream_t s) {
+  return lse ? launch_attn<D, 4, false, false, true, OUTF32>(p, s)
+             : launch_attn<D, 4, false, false, false, OUTF32>(p, s);
 }
 
 template <bool OUTF32>
 static hipError_t dispatch_shape(const AttnParams& p, int D, int C, bool sparse, bool res, bool lse,
                                  hipStream_t s) {
-  if (D == 128) {
-    return C == 128 ? dispatch_attn<128, 4, OUTF32>(p, sparse, res, lse, s)
-                    : dispatch_attn<128, 2, OUTF32>(p, sparse, res, lse, s);
+  if (!sparse) {
+    if (C != 128) return hipErrorInvalidValue;
+    return D == 128 ? dispatch_dense<128, OUTF32>(p, lse, s) : dispatch_dense<64, OUTF32>(p, lse, s);
   }
-  return C == 128 ? dispatch_attn<64, 4, OUTF32>(p, sparse, res, lse, s)
-                  : dispatch_attn<64, 2, OUTF32>(p, sparse, res, lse, s);
+  if (D == 128) {
+    return C == 128 ? dispatch_sparse<128, 4, OUTF32>(p, res, lse, s)
+                    : dispatch_sparse<128, 2, OUTF32>(p, res, lse, s);
+  }
+  return C == 128 ? dispatch_sparse<64, 4, OUTF32>(p, res, lse, s)
+                  : dispatch_sparse<64, 2, OUTF32>(p, res, lse, s);
 }
 
 hipError_t run_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
